@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Each test ties an oracle function to a page-printed example, a closed form,
+an invariant, a library routine on a special case, or pure-Python brute force
+on tiny inputs.  Together they are chosen so that a dropped term, a wrong
+sign or index, or a transposed operand anywhere in the oracle fails one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NAN = float("nan")
+
+
+# ----------------------------------------------------------------------------
+# helpers: a small paged problem built from logical K/V the test keeps
+# ----------------------------------------------------------------------------
+class Paged:
+    """Logical per-sequence K/V plus a shuffled paged cache holding them."""
+
+    def __init__(self, lens, Hkv, D, bs, dtype=torch.float32, seed=0, pool_extra=3,
+                 kmult=1.0):
+        g = torch.Generator().manual_seed(seed)
+        self.lens = list(lens)
+        self.bs, self.Hkv, self.D = bs, Hkv, D
+        need = [-(-L // bs) for L in lens]
+        self.nb = sum(need) + pool_extra
+        perm = torch.randperm(self.nb, generator=g)
+        self.table = torch.zeros(len(lens), max(need), dtype=torch.int32)
+        at = 0
+        for b, n in enumerate(need):
+            self.table[b, :n] = perm[at:at + n]
+            at += n
+        self.K = [(torch.randn(L, Hkv, D, generator=g) * kmult).to(dtype) for L in lens]
+        self.V = [torch.randn(L, Hkv, D, generator=g).to(dtype) for L in lens]
+        self.kc = torch.full((self.nb, bs, Hkv, D), NAN, dtype=dtype)
+        self.vc = torch.full((self.nb, bs, Hkv, D), NAN, dtype=dtype)
+        for b, L in enumerate(lens):
+            for j in range(L):
+                blk = int(self.table[b, j // bs])
+                self.kc[blk, j % bs] = self.K[b][j]
+                self.vc[blk, j % bs] = self.V[b][j]
+
+
+def brute_force(q, kc, vc, cu, lens, table, scale, causal, wl, cap, slopes, key_ranges=None):
+    """Pure-Python float64 attention, addressing the cache slot by slot."""
+    q = q.double().tolist()
+    kcl = kc.double().tolist()
+    vcl = vc.double().tolist()
+    T, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv, bs = len(kcl[0][0]), len(kcl[0])
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(T)]
+    lse = [[-math.inf] * T for _ in range(Hq)]
+    for b in range(len(lens)):
+        nq, L = cu[b + 1] - cu[b], lens[b]
+        for t in range(nq):
+            row, p = cu[b] + t, L - nq + t
+            for h in range(Hq):
+                g = (h * Hkv) // Hq
+                scores, vrows = [], []
+                for j in range(L):
+                    if causal and j > p:
+                        continue
+                    if wl >= 0 and j < p - wl:
+                        continue
+                    if key_ranges is not None and not (key_ranges[b][0] <= j < key_ranges[b][1]):
+                        continue
+                    blk, off = int(table[b][j // bs]), j % bs
+                    k = kcl[blk][off][g]
+                    s = scale * sum(q[row][h][d] * k[d] for d in range(D))
+                    if cap > 0:
+                        s = cap * math.tanh(s / cap)
+                    if slopes is not None:
+                        s -= float(slopes[h]) * abs(p - j)
+                    scores.append(s)
+                    vrows.append(vcl[blk][off][g])
+                if not scores:
+                    continue
+                m = max(scores)
+                ws = [math.exp(s - m) for s in scores]
+                tot = sum(ws)
+                for d in range(D):
+                    out[row][h][d] = sum(w * v[d] for w, v in zip(ws, vrows)) / tot
+                lse[h][row] = m + math.log(tot)
+    return torch.tensor(out, dtype=torch.float64), torch.tensor(lse, dtype=torch.float64)
+
+
+# ----------------------------------------------------------------------------
+# a1: scatter
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_scatter_bitexact_vs_numpy_fancy_index(dtype):
+    g = torch.Generator().manual_seed(7)
+    nb, bs, Hkv, D, T = 6, 16, 2, 64, 40
+    key = torch.randn(T + 3, Hkv, D, generator=g).to(dtype)      # padded rows
+    val = torch.randn(T + 3, Hkv, D, generator=g).to(dtype)
+    slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64)
+    slots[[3, 11, 30]] = -1                                        # padding slots
+    sentinel = 0x7E01 if dtype == torch.float16 else 0x7FC1
+    kc = torch.full((nb, bs, Hkv, D), 0, dtype=torch.int16).fill_(sentinel).view(dtype)
+    vc = kc.clone()
+    oracle.scatter(key, val, slots, kc, vc)
+
+    kn = np.full((nb * bs, Hkv, D), sentinel, dtype=np.uint16)
+    vn = kn.copy()
+    s = slots.numpy()
+    ok = s >= 0
+    kn[s[ok]] = key[:T].view(torch.int16).numpy().view(np.uint16)[ok]
+    vn[s[ok]] = val[:T].view(torch.int16).numpy().view(np.uint16)[ok]
+    assert np.array_equal(kc.view(torch.int16).numpy().view(np.uint16).reshape(nb * bs, Hkv, D), kn)
+    assert np.array_equal(vc.view(torch.int16).numpy().view(np.uint16).reshape(nb * bs, Hkv, D), vn)
+
+
+def test_gather_matches_page_block_table_example():
+    ex = json.load(open(os.path.join(GOLDEN, "metadata_examples.json")))["block_table"]
+    bs = ex["block_size"]
+    row = torch.tensor(ex["row"], dtype=torch.int32)
+    cache = torch.zeros(3, bs, 1, 2)
+    for blk in range(3):
+        for off in range(bs):
+            cache[blk, off, 0, 0] = blk
+            cache[blk, off, 0, 1] = off
+    rows = oracle.gather_sequence(cache, row, 3 * bs)
+    for tok, blk, off in ex["token_to_block_offset"]:
+        assert rows[tok, 0, 0] == blk and rows[tok, 0, 1] == off
+
+
+# ----------------------------------------------------------------------------
+# a2-a7: attention against brute force, SDPA and closed forms
+# ----------------------------------------------------------------------------
+BF_CASES = [
+    # lens, query_lens, Hq, Hkv, D, bs, causal, wl, cap, alibi
+    ([18, 41], [1, 1], 4, 2, 8, 16, True, -1, 0.0, False),        # decode, config-1 shape
+    ([23], [5], 4, 2, 8, 16, True, -1, 0.0, False),               # prefill chunk
+    ([23, 9], [5, 9], 4, 2, 8, 16, True, 6, 0.0, False),          # window
+    ([23, 9], [5, 3], 4, 1, 8, 16, True, -1, 1.0, False),         # strong softcap
+    ([23, 9], [5, 3], 6, 2, 8, 16, True, -1, 5.0, True),          # softcap + alibi, G=3
+    ([20, 7], [4, 7], 2, 2, 8, 32, False, -1, 0.0, True),         # non-causal alibi
+    ([33], [33], 8, 2, 4, 16, True, 3, 0.0, True),                # window + alibi
+]
+
+
+@pytest.mark.parametrize("case", BF_CASES)
+def test_attend_vs_brute_force(case):
+    lens, qlens, Hq, Hkv, D, bs, causal, wl, cap, alibi = case
+    P = Paged(lens, Hkv, D, bs, seed=len(lens) + D, kmult=2.0)
+    g = torch.Generator().manual_seed(11)
+    cu = W.cu_seqlens(qlens).tolist()
+    q = torch.randn(cu[-1], Hq, D, generator=g)
+    slopes = W.alibi_slopes(Hq) if alibi else None
+    scale = 1.0 / math.sqrt(D)
+    o, l = oracle.attend(q, P.kc, P.vc, cu, lens, P.table, scale, causal, wl, cap, slopes)
+    ob, lb = brute_force(q, P.kc, P.vc, cu, lens, P.table.tolist(), scale, causal, wl, cap, slopes)
+    assert torch.allclose(o, ob, atol=1e-12, rtol=1e-12)
+    assert torch.allclose(l, lb, atol=1e-12, rtol=1e-12)
+
+
+def _dense_mask(qlen, L, causal, wl):
+    p = torch.arange(L - qlen, L)[:, None]
+    j = torch.arange(L)[None, :]
+    m = torch.ones(qlen, L, dtype=torch.bool)
+    if causal:
+        m &= j <= p
+    if wl >= 0:
+        m &= p - j <= wl
+    return m
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+@pytest.mark.parametrize("wl", [-1, 37])
+def test_attend_vs_torch_sdpa(alibi, wl):
+    lens, qlens, Hq, Hkv, D, bs = [150, 97, 64], [150, 20, 1], 8, 2, 32, 16
+    P = Paged(lens, Hkv, D, bs, seed=3)
+    g = torch.Generator().manual_seed(5)
+    cu = W.cu_seqlens(qlens).tolist()
+    q = torch.randn(cu[-1], Hq, D, generator=g)
+    slopes = W.alibi_slopes(Hq) if alibi else None
+    scale = 0.3
+    o, l = oracle.attend(q, P.kc, P.vc, cu, lens, P.table, scale, True, wl, 0.0, slopes)
+    for b, (L, nq) in enumerate(zip(lens, qlens)):
+        K = P.K[b].double().repeat_interleave(Hq // Hkv, dim=1).permute(1, 0, 2)[None]
+        V = P.V[b].double().repeat_interleave(Hq // Hkv, dim=1).permute(1, 0, 2)[None]
+        Q = q[cu[b]:cu[b + 1]].double().permute(1, 0, 2)[None]
+        vis = _dense_mask(nq, L, True, wl)
+        bias = torch.zeros(Hq, nq, L, dtype=torch.float64)
+        if alibi:
+            dist = (torch.arange(L - nq, L)[:, None] - torch.arange(L)[None, :]).double()
+            bias = -slopes.double()[:, None, None] * dist[None]
+        bias = bias.masked_fill(~vis[None], float("-inf"))
+        ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=bias[None], scale=scale)[0]
+        assert torch.allclose(o[cu[b]:cu[b + 1]].permute(1, 0, 2), ref, atol=1e-10)
+        # LSE from the library's own logsumexp over the biased scores
+        s = scale * (Q[0] @ K[0].transpose(-1, -2)) + bias
+        assert torch.allclose(l[:, cu[b]:cu[b + 1]], torch.logsumexp(s, dim=-1), atol=1e-10)
+
+
+def test_zero_query_gives_mean_and_log_count():
+    lens, qlens = [40, 23], [6, 1]
+    P = Paged(lens, 2, 16, 16, seed=9)
+    cu = W.cu_seqlens(qlens).tolist()
+    q = torch.zeros(cu[-1], 4, 16)
+    o, l = oracle.attend(q, P.kc, P.vc, cu, lens, P.table, 0.7, True, 9, 0.0, None)
+    for b, (L, nq) in enumerate(zip(lens, qlens)):
+        for t in range(nq):
+            p = L - nq + t
+            lo = max(0, p - 9)
+            n = p - lo + 1
+            for h in range(4):
+                mean = P.V[b][lo:p + 1, h // 2].double().mean(dim=0)
+                assert torch.allclose(o[cu[b] + t, h], mean, atol=1e-12)
+                assert abs(float(l[h, cu[b] + t]) - math.log(n)) < 1e-12
+
+
+def test_zero_query_alibi_geometric_closed_form():
+    L = 50
+    P = Paged([L], 1, 8, 16, seed=2)
+    q = torch.zeros(L, 2, 8)
+    slopes = torch.tensor([0.5, 0.125])
+    o, l = oracle.attend(q, P.kc, P.vc, [0, L], [L], P.table, 1.0, True, -1, 0.0, slopes)
+    for h, sig in enumerate([0.5, 0.125]):
+        for p in range(L):
+            n = p + 1
+            closed = math.log((1 - math.exp(-sig * n)) / (1 - math.exp(-sig)))
+            assert abs(float(l[h, p]) - closed) < 1e-12
+
+
+def test_window_zero_returns_own_value_row():
+    lens = [37]
+    P = Paged(lens, 2, 16, 16, seed=4)
+    q = torch.randn(37, 2, 16)
+    o, _ = oracle.attend(q, P.kc, P.vc, [0, 37], lens, P.table, 1.0, True, 0, 0.0, None)
+    assert torch.equal(o, P.V[0].double())
+
+
+def test_single_key_returns_that_value():
+    P = Paged([1, 1], 1, 8, 16, seed=6)
+    q = torch.randn(2, 3, 8)
+    o, l = oracle.decode(q, P.kc, P.vc, [1, 1], P.table, 0.5)
+    for b in range(2):
+        assert torch.equal(o[b], P.V[b][0, 0].double().expand(3, 8))
+        sc = 0.5 * (q[b].double() @ P.K[b][0, 0].double())
+        assert torch.allclose(l[:, b], sc, atol=1e-14)
+
+
+def test_huge_softcap_equals_no_softcap():
+    P = Paged([30, 12], 2, 16, 16, seed=8)
+    q = torch.randn(2, 4, 16)
+    a = oracle.decode(q, P.kc, P.vc, [30, 12], P.table, 0.25, softcap=1e30)
+    b = oracle.decode(q, P.kc, P.vc, [30, 12], P.table, 0.25)
+    assert torch.allclose(a[0], b[0], atol=1e-12) and torch.allclose(a[1], b[1], atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one_via_constant_values():
+    P = Paged([64, 17], 2, 8, 16, seed=10)
+    P.vc[~torch.isnan(P.vc)] = 1.0
+    cu = [0, 64, 65]
+    q = torch.randn(65, 4, 8) * 3
+    o, _ = oracle.attend(q, P.kc, P.vc, cu, [64, 17], P.table, 1.0, True, 20, 7.0,
+                         W.alibi_slopes(4))
+    assert (o - 1.0).abs().max() < 1e-6
+
+
+# ----------------------------------------------------------------------------
+# paging, causality and decode/prefill invariants
+# ----------------------------------------------------------------------------
+def test_permuting_physical_blocks_is_bit_identical():
+    P = Paged([70, 33], 2, 16, 16, seed=12)
+    cu = [0, 70, 73]
+    q = torch.randn(73, 4, 16)
+    o1, l1 = oracle.attend(q, P.kc, P.vc, cu, [70, 33], P.table, 0.2, True, 25, 3.0, None)
+    perm = torch.randperm(P.nb)
+    kc2, vc2 = torch.empty_like(P.kc), torch.empty_like(P.vc)
+    kc2[perm] = P.kc
+    vc2[perm] = P.vc
+    table2 = perm[P.table.long()].to(torch.int32)
+    o2, l2 = oracle.attend(q, kc2, vc2, cu, [70, 33], table2, 0.2, True, 25, 3.0, None)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_identity_table_equals_dense_attention():
+    L, Hkv, D = 40, 1, 8
+    P = Paged([L], Hkv, D, 64, seed=13, pool_extra=0)
+    assert P.nb == 1
+    q = torch.randn(L, 1, D)
+    o, _ = oracle.attend(q, P.kc, P.vc, [0, L], [L], torch.zeros(1, 1, dtype=torch.int32),
+                         0.5, True)
+    K, V = P.K[0][:, 0].double(), P.V[0][:, 0].double()
+    s = 0.5 * q[:, 0].double() @ K.T
+    s = s.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+    assert torch.allclose(o[:, 0], torch.softmax(s, dim=-1) @ V, atol=1e-12)
+
+
+def test_causal_output_ignores_future_keys():
+    P = Paged([48], 2, 16, 16, seed=14)
+    q = torch.randn(48, 4, 16)
+    o1, l1 = oracle.attend(q, P.kc, P.vc, [0, 48], [48], P.table, 0.3, True)
+    kc, vc = P.kc.clone(), P.vc.clone()
+    for j in range(30, 48):
+        blk = int(P.table[0, j // 16])
+        kc[blk, j % 16] += 5.0
+        vc[blk, j % 16] -= 3.0
+    o2, l2 = oracle.attend(q, kc, vc, [0, 48], [48], P.table, 0.3, True)
+    assert torch.equal(o1[:30], o2[:30]) and torch.equal(l1[:, :30], l2[:, :30])
+    assert not torch.equal(o1[30:], o2[30:])
+
+
+def test_decode_equals_last_row_of_prefill():
+    lens = [57, 16]
+    P = Paged(lens, 2, 16, 16, seed=15)
+    q = torch.randn(sum(lens), 4, 16)
+    cu = W.cu_seqlens(lens).tolist()
+    op, lp = oracle.attend(q, P.kc, P.vc, cu, lens, P.table, 0.25, True, 20, 4.0,
+                           W.alibi_slopes(4))
+    last = [cu[b + 1] - 1 for b in range(2)]
+    od, ld = oracle.decode(q[last], P.kc, P.vc, lens, P.table, 0.25, 20, 4.0, W.alibi_slopes(4))
+    assert torch.allclose(od, op[last], atol=1e-13) and torch.allclose(ld, lp[:, last], atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# a8-a9: split boundaries and merge
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("L,S,bs", [(131072, 32, 16), (1000, 3, 16), (17, 4, 16), (5, 8, 32),
+                                    (4096, 7, 32)])
+def test_split_bounds_partition_block_aligned(L, S, bs):
+    b = oracle.split_bounds(L, S, bs)
+    assert len(b) == S and b[0][0] == 0 and b[-1][1] == L
+    for (lo, hi), (lo2, _) in zip(b, b[1:]):
+        assert hi == lo2 and lo <= hi and (lo % bs == 0 or lo == hi == L)
+    if (L, S) == (131072, 32):
+        assert all(hi - lo == 4096 for lo, hi in b)
+
+
+@pytest.mark.parametrize("S", [2, 3, 32])
+def test_split_then_merge_equals_unsplit(S):
+    lens = [200, 45, 16, 1]
+    P = Paged(lens, 2, 16, 16, seed=16)
+    q = torch.randn(4, 8, 16)
+    slopes = W.alibi_slopes(8)
+    po, pl = oracle.decode_splits(q, P.kc, P.vc, lens, P.table, 0.25, S, 60, 6.0, slopes)
+    mo, ml = oracle.merge(po, pl)
+    o, l = oracle.decode(q, P.kc, P.vc, lens, P.table, 0.25, 60, 6.0, slopes)
+    assert torch.allclose(mo, o, atol=1e-12) and torch.allclose(ml, l, atol=1e-12)
+
+
+def test_merge_identical_states_adds_log2():
+    o = torch.randn(1, 5, 3, 8, dtype=torch.float64)
+    l = torch.randn(1, 3, 5, dtype=torch.float64)
+    mo, ml = oracle.merge(torch.cat([o, o]), torch.cat([l, l]))
+    assert torch.allclose(mo, o[0], atol=1e-14)
+    assert torch.allclose(ml, l[0] + math.log(2.0), atol=1e-14)
+
+
+def test_merge_with_empty_part_is_identity_and_all_empty_is_zero():
+    o = torch.randn(1, 4, 2, 8, dtype=torch.float64)
+    l = torch.randn(1, 2, 4, dtype=torch.float64)
+    empty_o = torch.zeros_like(o)
+    empty_l = torch.full_like(l, float("-inf"))
+    mo, ml = oracle.merge(torch.cat([empty_o, o, empty_o]), torch.cat([empty_l, l, empty_l]))
+    assert torch.equal(mo, o[0]) and torch.equal(ml, l[0])
+    zo, zl = oracle.merge(torch.cat([empty_o, empty_o]), torch.cat([empty_l, empty_l]))
+    assert torch.equal(zo, torch.zeros_like(o[0])) and torch.isneginf(zl).all()
+
+
+def test_merge_two_parts_matches_softmax_over_union():
+    # two disjoint key sets; the merge of their states is attention over both
+    g = torch.Generator().manual_seed(17)
+    s1, s2 = torch.randn(7, generator=g, dtype=torch.float64), torch.randn(4, generator=g, dtype=torch.float64)
+    v1, v2 = torch.randn(7, 3, generator=g, dtype=torch.float64), torch.randn(4, 3, generator=g, dtype=torch.float64)
+    o1 = torch.softmax(s1, 0) @ v1
+    o2 = torch.softmax(s2, 0) @ v2
+    parts_o = torch.stack([o1, o2])[:, None, None, :]
+    parts_l = torch.stack([torch.logsumexp(s1, 0), torch.logsumexp(s2, 0)])[:, None, None]
+    mo, ml = oracle.merge(parts_o, parts_l)
+    s = torch.cat([s1, s2])
+    assert torch.allclose(mo[0, 0], torch.softmax(s, 0) @ torch.cat([v1, v2]), atol=1e-14)
+    assert abs(float(ml[0, 0]) - float(torch.logsumexp(s, 0))) < 1e-14
