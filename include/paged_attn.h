@@ -1,0 +1,179 @@
+/*
+ * paged_attn.h — C ABI of libpagedattn.so: attention over a paged KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The cache has the shape (2, num_blocks, block_size, num_kv_heads,
+ * head_size); key_cache and value_cache below are its two halves, each a
+ * contiguous [num_blocks, block_size, num_kv_heads, head_size] array
+ * [vLLM flash_attn.py (e2f56c3), FlashAttentionBackend.get_kv_cache_shape;
+ * FlashAttentionImpl.forward, kv_cache.unbind(0)].  A sequence's logical
+ * token j lives at (block_table[b][j / block_size], j % block_size)
+ * [Aphrodite flash_attn.py, FlashAttentionMetadata, block_tables].
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers, except where a parameter says
+ *    otherwise.  Integer sizes and scalars are passed by value from the host.
+ *  - The caller owns every buffer, outputs included; the library allocates
+ *    nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronising.
+ *  - Return value: PA_OK, or a negative code.  Arguments are validated on the
+ *    host before anything is enqueued; on a validation error nothing is
+ *    written.  pa_last_error() gives a message for the last failure of the
+ *    calling thread.
+ *  - Contents of device arrays (slot ids, block ids, lengths) are trusted:
+ *    an out-of-range block id or slot is undefined behaviour.
+ *  - dtype of q / key / value / caches / out: PA_F16 or PA_BF16.  All
+ *    arithmetic is fp32; outputs are rounded to nearest-even.
+ *  - head_size must be 64, 128 or 256; block_size a positive multiple of 16
+ *    and at most 256; num_heads a multiple of num_kv_heads.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F32 = 2 } pa_dtype_t;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,      /* bad argument (NULL pointer, inconsistent sizes) */
+  PA_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement */
+  PA_ERR_HIP = -3           /* the HIP runtime reported an error on launch */
+};
+
+/*
+ * reshape_and_cache — write the K and V rows of new tokens into their cache
+ * slots [vLLM flash_attn.py (e2f56c3), FlashAttentionImpl.forward, the
+ * reshape_and_cache_flash call; Aphrodite flash_attn.py, the
+ * reshape_and_cache_flash custom op].
+ *
+ *   key, value      [>= num_tokens rows, num_kv_heads, head_size]; row i
+ *                   starts at key + i * key_token_stride (elements); heads
+ *                   and head elements are contiguous within a row.
+ *   key_cache,
+ *   value_cache     [num_blocks, block_size, num_kv_heads, head_size].
+ *   slot_mapping    int64 [num_tokens]; token i goes to block
+ *                   slot / block_size, offset slot % block_size.  A negative
+ *                   slot is padding and is skipped.  num_tokens is the length
+ *                   of slot_mapping; key/value may hold more (padded) rows.
+ *   Copies are bit-exact (kv_cache_dtype "auto": no conversion).  Two tokens
+ *   mapped to the same slot race (the caller must not do that).
+ *   num_tokens == 0 is a no-op.
+ */
+int reshape_and_cache(const void* key, const void* value,
+                      int64_t key_token_stride, int64_t value_token_stride,
+                      void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int64_t num_tokens,
+                      int64_t num_blocks, int block_size, int num_kv_heads,
+                      int head_size, pa_dtype_t dtype, void* stream);
+
+/*
+ * paged_attn_prefill — variable-length attention of new query tokens over
+ * the paged cache (prefill chunks, or any mix of query lengths)
+ * [vLLM flash_attn.py (e2f56c3), FlashAttentionImpl.forward, the
+ * flash_attn_varlen_func call with block_table and seqused_k].
+ *
+ *   out             [total_q, num_heads, head_size] (dtype).
+ *   lse             nullable; fp32 [num_heads, total_q], natural log.
+ *   q               [total_q, num_heads, head_size] (dtype), contiguous.
+ *   cu_seqlens_q    int32 [num_seqs + 1]: queries of sequence b are rows
+ *                   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *   seq_lens        int32 [num_seqs]: keys of sequence b (context + its new
+ *                   tokens, which must already be in the cache); the query
+ *                   rows are the LAST positions: row t of b sits at position
+ *                   p = seq_lens[b] - q_len_b + t.
+ *   block_table     int32, row b at block_table + b * block_table_stride.
+ *   max_seqlen_q    host upper bound of the query lengths (sizes the grid).
+ *   max_seqlen_k    host upper bound of seq_lens.
+ *   scale           softmax scale applied to q.k.
+ *   causal          nonzero: key j visible to position p iff j <= p.
+ *   window_left     -1: none; else also require j >= p - window_left (a
+ *                   sliding window w is passed as w - 1).
+ *   softcap         0: off; else s = softcap * tanh(s / softcap) on the
+ *                   scaled score.
+ *   alibi_slopes    nullable; fp32 [num_heads]; adds -slope_h * |p - j|
+ *                   after the softcap.
+ *   Query head h reads KV head h / (num_heads / num_kv_heads).
+ *   A query that sees no key gets out = 0 and lse = -inf.
+ */
+int paged_attn_prefill(void* out, float* lse, const void* q,
+                       const void* key_cache, const void* value_cache,
+                       const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                       const int32_t* block_table, int64_t block_table_stride,
+                       int num_seqs, int64_t total_q, int max_seqlen_q,
+                       int max_seqlen_k, int num_heads, int num_kv_heads,
+                       int head_size, int block_size, int64_t num_blocks,
+                       float scale, int causal, int window_left, float softcap,
+                       const float* alibi_slopes, pa_dtype_t dtype,
+                       void* stream);
+
+/*
+ * paged_attn_decode — one query token per sequence over the paged cache,
+ * optionally split along the keys [Aphrodite flash_attn.py,
+ * FlashAttentionImpl.forward, the flash_attn_with_kvcache decode call;
+ * vLLM flash_attn.py (e2f56c3), FlashAttentionMetadataBuilder, num_splits
+ * and its [num_splits, num_heads, num_tokens, head_size] intermediates].
+ *
+ *   q               [num_seqs, num_heads, head_size] (dtype); the query of
+ *                   sequence b sits at position seq_lens[b] - 1.
+ *   seq_lens        int32 [num_seqs]; block_table as for prefill.
+ *   num_splits == 1 writes out [num_seqs, num_heads, head_size] (dtype) and,
+ *                   if lse != NULL, lse fp32 [num_heads, num_seqs].
+ *   num_splits  > 1 writes only part_out fp32 [num_splits, num_seqs,
+ *                   num_heads, head_size] and part_lse fp32 [num_splits,
+ *                   num_heads, num_seqs]; out and lse are not touched (may be
+ *                   NULL).  Split p of sequence b covers keys
+ *                   [p*c, min((p+1)*c, L)) with c = block_size *
+ *                   ceil(ceil(L / num_splits) / block_size); an empty split
+ *                   writes part_out = 0, part_lse = -inf.  Combine with
+ *                   merge_attn_states(out, lse, part_out, part_lse,
+ *                   num_splits, num_seqs, num_heads, head_size, PA_F32, ...).
+ *   window_left, softcap, alibi_slopes as for prefill.  num_splits <= 256.
+ *   num_heads / num_kv_heads must be at most 16.
+ */
+int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
+                      const void* q, const void* key_cache,
+                      const void* value_cache, const int32_t* seq_lens,
+                      const int32_t* block_table, int64_t block_table_stride,
+                      int num_seqs, int max_seq_len, int num_heads,
+                      int num_kv_heads, int head_size, int block_size,
+                      int64_t num_blocks, float scale, int window_left,
+                      float softcap, const float* alibi_slopes, int num_splits,
+                      pa_dtype_t dtype, void* stream);
+
+/*
+ * merge_attn_states — combine partial attention results by their
+ * log-sum-exp [vLLM flash_attn.py (e2f56c3), cascade_attention and
+ * _forward_with_dcp, merge_attn_states(out, a_out, a_lse, b_out, b_lse)].
+ *
+ *   parts_out       [num_parts, num_tokens, num_heads, head_size] in
+ *                   parts_dtype (PA_F32, PA_F16 or PA_BF16).
+ *   parts_lse       fp32 [num_parts, num_heads, num_tokens], natural log.
+ *   out             [num_tokens, num_heads, head_size] in out_dtype
+ *                   (PA_F32, PA_F16 or PA_BF16).
+ *   out_lse         nullable; fp32 [num_heads, num_tokens].
+ *   Per (t, h): M = max_p lse_p, w_p = exp(lse_p - M),
+ *   out = sum_p w_p out_p / sum_p w_p, out_lse = M + ln(sum_p w_p); if every
+ *   part is -inf, out = 0 and out_lse = -inf.  1 <= num_parts <= 256.
+ */
+int merge_attn_states(void* out, float* out_lse, const void* parts_out,
+                      const float* parts_lse, int num_parts,
+                      int64_t num_tokens, int num_heads, int head_size,
+                      pa_dtype_t parts_dtype, pa_dtype_t out_dtype,
+                      void* stream);
+
+/* Message describing the last non-OK return on the calling thread ("" if
+ * none).  The string is owned by the library and valid until the next call
+ * on this thread. */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,157 @@
+"""Paged-KV attention for AMD MI355X (gfx950): thin Python binding.
+
+Every function here only marshals arguments (torch tensors -> device
+pointers and sizes, the current HIP stream) and calls the entry point of the
+same name in ``libpagedattn.so`` (declared in ``include/paged_attn.h``).  All
+work runs in the library's HIP kernels; there is no fallback.  Importing the
+package fails if the library has not been built (``python -m
+paged_kv_attention_29_amd.build`` or ``__graft_entry__.build()``).
+
+Tensors are caller-owned and must live on the GPU; the library allocates
+nothing.  Shapes follow the C header:
+  q / out                [tokens, num_heads, head_size], fp16 or bf16
+  key_cache, value_cache [num_blocks, block_size, num_kv_heads, head_size]
+  block_table            int32 [num_seqs, max_blocks]
+  slot_mapping           int64 [num_tokens]
+  lse                    fp32 [num_heads, tokens]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PagedAttnError",
+    "reshape_and_cache",
+    "paged_attn_prefill",
+    "paged_attn_decode",
+    "merge_attn_states",
+    "pa_last_error",
+    "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpagedattn.so")
+
+PA_F16, PA_BF16, PA_F32 = 0, 1, 2
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
+
+_vp, _i64, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with `python -m paged_kv_attention_29_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    lib.reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
+                                      _i32, _i32, _vp]
+    lib.paged_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32,
+                                       _f32, _vp, _i32, _vp]
+    lib.paged_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
+                                      _i32, _i32, _vp]
+    lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
+    for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def pa_last_error() -> str:
+    return lib.pa_last_error().decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != PA_OK:
+        raise PagedAttnError(fn, rc, pa_last_error())
+
+
+def _code(t: torch.dtype) -> int:
+    if t == torch.float16:
+        return PA_F16
+    if t == torch.bfloat16:
+        return PA_BF16
+    if t == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write key/value rows [i] into slot slot_mapping[i]; negative slots skip."""
+    nb, bs, hkv, d = key_cache.shape
+    _check("reshape_and_cache", lib.reshape_and_cache(
+        _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_cache),
+        _ptr(value_cache), _ptr(slot_mapping), slot_mapping.numel(), nb, bs, hkv, d,
+        _code(key_cache.dtype), _stream(stream)))
+
+
+def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                       seq_lens: torch.Tensor, block_table: torch.Tensor, max_seqlen_q: int,
+                       max_seqlen_k: int, scale: float, causal: bool = True,
+                       window_left: int = -1, softcap: float = 0.0,
+                       alibi_slopes: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    total_q, hq, d = q.shape
+    nb, bs, hkv, _ = key_cache.shape
+    _check("paged_attn_prefill", lib.paged_attn_prefill(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
+        _ptr(seq_lens), _ptr(block_table), block_table.stride(0), seq_lens.numel(), total_q,
+        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
+        int(window_left), float(softcap), _ptr(alibi_slopes), _code(q.dtype), _stream(stream)))
+    return out
+
+
+def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, seq_lens: torch.Tensor,
+                      block_table: torch.Tensor, max_seq_len: int, scale: float,
+                      window_left: int = -1, softcap: float = 0.0,
+                      alibi_slopes: Optional[torch.Tensor] = None, num_splits: int = 1,
+                      part_out: Optional[torch.Tensor] = None,
+                      part_lse: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = key_cache.shape
+    _check("paged_attn_decode", lib.paged_attn_decode(
+        _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse), _ptr(q), _ptr(key_cache),
+        _ptr(value_cache), _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b,
+        int(max_seq_len), hq, hkv, d, bs, nb, float(scale), int(window_left), float(softcap),
+        _ptr(alibi_slopes), int(num_splits), _code(q.dtype), _stream(stream)))
+
+
+def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: torch.Tensor,
+                      out_lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """parts_out [S, T, H, D], parts_lse [S, H, T] -> out [T, H, D] (+ out_lse [H, T])."""
+    s, t, h, d = parts_out.shape
+    _check("merge_attn_states", lib.merge_attn_states(
+        _ptr(out), _ptr(out_lse), _ptr(parts_out), _ptr(parts_lse), s, t, h, d,
+        _code(parts_out.dtype), _code(out.dtype), _stream(stream)))
+    return out

@@ -1,0 +1,241 @@
+// C ABI of libpagedattn.so (declared in include/paged_attn.h): host-side
+// argument validation, then one kernel launch on the caller's stream.
+// Validation mirrors the checks the backends make before calling their
+// kernels (vLLM flash_attn.py (e2f56c3): block_size multiple of 16 in
+// get_kv_cache_shape, fp16/bf16 in supported_dtypes, output buffer required
+// in FlashAttentionImpl.forward; vLLM 0.9.0.1 flash_attn API docs:
+// num_heads divisible by num_kv_heads).  Nothing is enqueued when a check
+// fails.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/paged_attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int hip_result(int rc, const char* what) {
+  if (rc == 0) return ok();
+  return fail(PA_ERR_HIP, "%s: kernel launch failed: %s", what,
+              hipGetErrorString(hipGetLastError()));
+}
+
+bool is_16bit(pa_dtype_t t) { return t == PA_F16 || t == PA_BF16; }
+
+// shape checks shared by every entry point that touches the cache
+int check_cache_shape(const char* fn, int block_size, int num_kv_heads, int head_size,
+                      pa_dtype_t dtype) {
+  if (!is_16bit(dtype))
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_F16 or PA_BF16 (got %d)", fn, (int)dtype);
+  if (block_size <= 0 || block_size % 16 != 0)
+    return fail(PA_ERR_INVALID, "%s: block_size must be a positive multiple of 16 (got %d)", fn,
+                block_size);
+  if (block_size > 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size above 256 is not supported (got %d)", fn,
+                block_size);
+  if (num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_kv_heads must be positive (got %d)", fn, num_kv_heads);
+  if (head_size != 64 && head_size != 128 && head_size != 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_size must be 64, 128 or 256 (got %d)", fn, head_size);
+  return PA_OK;
+}
+
+int check_attn_common(const char* fn, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_size, int block_size, int64_t num_blocks, float scale,
+                      int window_left, float softcap, pa_dtype_t dtype, const void* q,
+                      const void* kc, const void* vc, const int32_t* seq_lens,
+                      const int32_t* block_table, int64_t bt_stride) {
+  int rc = check_cache_shape(fn, block_size, num_kv_heads, head_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "%s: num_seqs must be >= 0", fn);
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                fn, num_heads, num_kv_heads);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale must be finite", fn);
+  if (window_left < -1) return fail(PA_ERR_INVALID, "%s: window_left must be >= -1", fn);
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap))
+    return fail(PA_ERR_INVALID, "%s: softcap must be finite and >= 0 (0 = off)", fn);
+  if (num_seqs > 0) {
+    if (q == nullptr || kc == nullptr || vc == nullptr || seq_lens == nullptr ||
+        block_table == nullptr)
+      return fail(PA_ERR_INVALID, "%s: NULL input pointer", fn);
+    if (bt_stride <= 0) return fail(PA_ERR_INVALID, "%s: block_table_stride must be positive", fn);
+    if (num_blocks <= 0) return fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int reshape_and_cache(const void* key, const void* value, int64_t key_token_stride,
+                      int64_t value_token_stride, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                      int block_size, int num_kv_heads, int head_size, pa_dtype_t dtype,
+                      void* stream) {
+  const char* fn = "reshape_and_cache";
+  int rc = check_cache_shape(fn, block_size, num_kv_heads, head_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: num_tokens must be >= 0", fn);
+  if (num_tokens == 0) return ok();
+  if (key == nullptr || value == nullptr || key_cache == nullptr || value_cache == nullptr ||
+      slot_mapping == nullptr)
+    return fail(PA_ERR_INVALID, "%s: NULL pointer", fn);
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_token_stride < row || value_token_stride < row)
+    return fail(PA_ERR_INVALID, "%s: token strides (%lld, %lld) must be >= num_kv_heads*head_size (%lld)",
+                fn, (long long)key_token_stride, (long long)value_token_stride, (long long)row);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
+  return hip_result(pa::launch_reshape_and_cache(key, value, key_token_stride, value_token_stride,
+                                                 key_cache, value_cache, slot_mapping, num_tokens,
+                                                 static_cast<int>(row),
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cache,
+                       const void* value_cache, const int32_t* cu_seqlens_q,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int64_t block_table_stride, int num_seqs, int64_t total_q,
+                       int max_seqlen_q, int max_seqlen_k, int num_heads, int num_kv_heads,
+                       int head_size, int block_size, int64_t num_blocks, float scale, int causal,
+                       int window_left, float softcap, const float* alibi_slopes,
+                       pa_dtype_t dtype, void* stream) {
+  const char* fn = "paged_attn_prefill";
+  int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, scale, window_left, softcap, dtype, q, key_cache,
+                             value_cache, seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
+  if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(PA_ERR_INVALID, "%s: total_q / max_seqlen_q / max_seqlen_k must be >= 0", fn);
+  if (num_seqs > 0 && cu_seqlens_q == nullptr)
+    return fail(PA_ERR_INVALID, "%s: NULL cu_seqlens_q", fn);
+  if (num_heads / num_kv_heads > 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 128 query heads per KV head", fn);
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  pa::AttnParams p{};
+  p.out = out;
+  p.lse = lse;
+  p.q = q;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.block_table_stride = block_table_stride;
+  p.num_seqs = num_seqs;
+  p.total_q = total_q;
+  p.max_seqlen_q = max_seqlen_q;
+  p.max_seqlen_k = max_seqlen_k;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_size = head_size;
+  p.block_size = block_size;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.softcap = softcap;
+  p.alibi_slopes = alibi_slopes;
+  p.num_splits = 1;
+  p.dtype = static_cast<pa::Dtype>(dtype);
+  return hip_result(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                      const void* key_cache, const void* value_cache, const int32_t* seq_lens,
+                      const int32_t* block_table, int64_t block_table_stride, int num_seqs,
+                      int max_seq_len, int num_heads, int num_kv_heads, int head_size,
+                      int block_size, int64_t num_blocks, float scale, int window_left,
+                      float softcap, const float* alibi_slopes, int num_splits,
+                      pa_dtype_t dtype, void* stream) {
+  const char* fn = "paged_attn_decode";
+  int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, scale, window_left, softcap, dtype, q, key_cache,
+                             value_cache, seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  if (num_splits < 1 || num_splits > 256)
+    return fail(PA_ERR_INVALID, "%s: num_splits must be in [1, 256] (got %d)", fn, num_splits);
+  if (num_splits == 1 && out == nullptr)
+    return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
+  if (num_splits > 1 && (part_out == nullptr || part_lse == nullptr))
+    return fail(PA_ERR_INVALID, "%s: num_splits > 1 needs part_out and part_lse", fn);
+  if (num_heads / num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
+  if (max_seq_len < 0) return fail(PA_ERR_INVALID, "%s: max_seq_len must be >= 0", fn);
+  if (num_seqs == 0) return ok();
+  pa::AttnParams p{};
+  p.out = out;
+  p.lse = lse;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.q = q;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.block_table_stride = block_table_stride;
+  p.num_seqs = num_seqs;
+  p.total_q = num_seqs;
+  p.max_seqlen_q = 1;
+  p.max_seqlen_k = max_seq_len;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_size = head_size;
+  p.block_size = block_size;
+  p.scale = scale;
+  p.causal = 1;
+  p.window_left = window_left;
+  p.softcap = softcap;
+  p.alibi_slopes = alibi_slopes;
+  p.num_splits = num_splits;
+  p.dtype = static_cast<pa::Dtype>(dtype);
+  return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+int merge_attn_states(void* out, float* out_lse, const void* parts_out, const float* parts_lse,
+                      int num_parts, int64_t num_tokens, int num_heads, int head_size,
+                      pa_dtype_t parts_dtype, pa_dtype_t out_dtype, void* stream) {
+  const char* fn = "merge_attn_states";
+  auto dtype_ok = [](pa_dtype_t t) { return t == PA_F16 || t == PA_BF16 || t == PA_F32; };
+  if (!dtype_ok(parts_dtype) || !dtype_ok(out_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtypes must be PA_F32, PA_F16 or PA_BF16", fn);
+  if (head_size != 64 && head_size != 128 && head_size != 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_size must be 64, 128 or 256 (got %d)", fn, head_size);
+  if (num_parts < 1 || num_parts > 256)
+    return fail(PA_ERR_INVALID, "%s: num_parts must be in [1, 256] (got %d)", fn, num_parts);
+  if (num_tokens < 0 || num_heads <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_tokens must be >= 0 and num_heads > 0", fn);
+  if (num_tokens == 0) return ok();
+  if (out == nullptr || parts_out == nullptr || parts_lse == nullptr)
+    return fail(PA_ERR_INVALID, "%s: NULL pointer", fn);
+  return hip_result(pa::launch_merge(out, out_lse, parts_out, parts_lse, num_parts, num_tokens,
+                                     num_heads, head_size, static_cast<pa::Dtype>(parts_dtype),
+                                     static_cast<pa::Dtype>(out_dtype),
+                                     static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Shared device helpers for the gfx950 paged-attention kernels: 16-bit
+// storage types, fp32 conversions, MFMA wrappers and wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// 16-bit element types.  Storage is always the raw 16-bit pattern.
+// ---------------------------------------------------------------------------
+struct BF16 {
+  static __device__ __forceinline__ float to_float(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+  }
+  // round to nearest even; NaN stays NaN
+  static __device__ __forceinline__ uint16_t from_float(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  }
+  // two floats -> packed pair (lo in bits 0..15)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return static_cast<uint32_t>(from_float(lo)) | (static_cast<uint32_t>(from_float(hi)) << 16);
+  }
+  // D[16x16] += A[16x32] * B[32x16]; operands are 8 elements per lane
+  static __device__ __forceinline__ v4f mfma16x16x32(v8s a, v8s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+  // D[32x32] += A[32x16] * B[16x32]
+  static __device__ __forceinline__ v16f mfma32x32x16(v8s a, v8s b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+  // D[16x16] += A[16x16] * B[16x16]; 4 elements per lane
+  static __device__ __forceinline__ v4f mfma16x16x16(v4s a, v4s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  static __device__ __forceinline__ float to_float(uint16_t x) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, x));
+  }
+  static __device__ __forceinline__ uint16_t from_float(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return static_cast<uint32_t>(from_float(lo)) | (static_cast<uint32_t>(from_float(hi)) << 16);
+  }
+  static __device__ __forceinline__ v4f mfma16x16x32(v8s a, v8s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                  __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v16f mfma32x32x16(v8s a, v8s b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                  __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4f mfma16x16x16(v4s a, v4s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, a),
+                                                 __builtin_bit_cast(v4h, b), c, 0, 0, 0);
+  }
+};
+
+struct F32 {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+};
+
+// ---------------------------------------------------------------------------
+// wave64 cross-lane helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  int lane = __lane_id();
+  int src = lane ^ mask;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+// exp2 of a finite-or--inf argument (v_exp_f32); exp2(-inf) = 0
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh from exp: tanh(x) = sign(x) * (1 - 2 / (exp(2|x|) + 1)); exact limits
+// at +-inf, absolute error a few ulp of 1 near 0.
+__device__ __forceinline__ float tanh_f32(float x) {
+  float ax = fabsf(x);
+  float e = fast_exp2(2.0f * kLog2e * ax);
+  float t = 1.0f - 2.0f / (e + 1.0f);
+  return copysignf(t, x);
+}
+
+// Order LDS writes before later LDS reads of other lanes of the same wave
+// (LDS accesses of one wave are executed in order; this only stops the
+// compiler from moving memory operations across the point).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace pa

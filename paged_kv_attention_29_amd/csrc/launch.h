@@ -1,0 +1,53 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the
+// C-ABI layer before these are called; each returns 0 or -3 (HIP error).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dtype { kF16 = 0, kBF16 = 1, kF32 = 2 };
+
+int launch_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
+                             int64_t value_stride, void* key_cache, void* value_cache,
+                             const int64_t* slots, int64_t num_tokens, int row_elems,
+                             hipStream_t stream);
+
+int launch_merge(void* out, float* out_lse, const void* parts, const float* parts_lse,
+                 int num_parts, int64_t num_tokens, int num_heads, int head_size,
+                 Dtype parts_dtype, Dtype out_dtype, hipStream_t stream);
+
+struct AttnParams {
+  void* out;                    // [T, Hq, D] dtype   (decode S == 1 / prefill)
+  float* lse;                   // [Hq, T] or null
+  float* part_out;              // decode S > 1: [S, B, Hq, D]
+  float* part_lse;              // decode S > 1: [S, Hq, B]
+  const void* q;                // [T, Hq, D]
+  const void* key_cache;        // [nb, bs, Hkv, D]
+  const void* value_cache;
+  const int32_t* cu_seqlens_q;  // prefill: [B + 1]
+  const int32_t* seq_lens;      // [B]
+  const int32_t* block_table;
+  int64_t block_table_stride;
+  int num_seqs;
+  int64_t total_q;
+  int max_seqlen_q;
+  int max_seqlen_k;
+  int num_heads;
+  int num_kv_heads;
+  int head_size;
+  int block_size;
+  float scale;
+  int causal;
+  int window_left;
+  float softcap;
+  const float* alibi_slopes;
+  int num_splits;
+  Dtype dtype;
+};
+
+int launch_decode(const AttnParams& p, hipStream_t stream);
+int launch_prefill(const AttnParams& p, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every entry point its header declares,
+and rejects invalid arguments on the host before touching a GPU (no GPU
+needed: every call here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode",
+               "merge_attn_states", "pa_last_error"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    import paged_kv_attention_29_amd as pa
+    for fn in _declared_functions():
+        assert hasattr(pa.lib, fn), fn
+    out = os.popen(f"nm -D --defined-only {pa.library_path}").read()
+    for fn in _declared_functions():
+        assert re.search(rf"\bT {fn}$", out, flags=re.M), fn
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import paged_kv_attention_29_amd as pa
+    return pa
+
+
+def _decode(pa, **kw):
+    args = dict(out=1, lse=None, part_out=None, part_lse=None, q=1, kc=1, vc=1, seq_lens=1,
+                bt=1, bt_stride=4, num_seqs=2, max_seq_len=10, hq=4, hkv=2, d=64, bs=16, nb=8,
+                scale=0.125, wl=-1, cap=0.0, alibi=None, splits=1, dtype=pa.PA_F16)
+    args.update(kw)
+    return pa.lib.paged_attn_decode(*args.values(), None)
+
+
+def _prefill(pa, **kw):
+    args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
+                num_seqs=1, total_q=5, mq=5, mk=23, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
+                causal=1, wl=-1, cap=0.0, alibi=None, dtype=pa.PA_F16)
+    args.update(kw)
+    return pa.lib.paged_attn_prefill(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=24), -1), (dict(bs=0), -1), (dict(bs=512), -2),
+    (dict(hq=6, hkv=4), -1), (dict(d=96), -2), (dict(dtype=2), -2), (dict(dtype=7), -2),
+    (dict(out=None), -1), (dict(splits=2), -1), (dict(splits=0), -1), (dict(splits=300), -1),
+    (dict(hq=34, hkv=2), -2), (dict(wl=-2), -1), (dict(cap=-1.0), -1),
+    (dict(scale=float("inf")), -1), (dict(q=None), -1), (dict(bt_stride=0), -1),
+])
+def test_decode_validation(lib, kw, code):
+    assert _decode(lib, **kw) == code
+    assert lib.pa_last_error().startswith("paged_attn_decode")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=8), -1), (dict(hq=5, hkv=2), -1), (dict(d=32), -2), (dict(out=None), -1),
+    (dict(cu=None), -1), (dict(total_q=-1), -1), (dict(dtype=2), -2),
+])
+def test_prefill_validation(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+
+
+def test_empty_calls_are_noops(lib):
+    assert _decode(lib, num_seqs=0, q=None, kc=None, vc=None, seq_lens=None, bt=None) == 0
+    assert _prefill(lib, num_seqs=0, q=None, kc=None, vc=None, seq_lens=None, bt=None, cu=None,
+                    total_q=0) == 0
+    assert lib.pa_last_error() == ""
+
+
+def test_reshape_and_cache_validation(lib):
+    f = lib.lib.reshape_and_cache
+    assert f(1, 1, 100, 128, 1, 1, 1, 4, 8, 16, 2, 64, lib.PA_BF16, None) == -1   # short stride
+    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 20, 2, 64, lib.PA_BF16, None) == -1   # block size
+    assert f(1, 1, 128, 128, 1, 1, None, 4, 8, 16, 2, 64, lib.PA_BF16, None) == -1
+    assert f(None, None, 128, 128, None, None, None, 0, 8, 16, 2, 64, lib.PA_BF16, None) == 0
+    assert f(1, 1, 128, 128, 1, 1, 1, -1, 8, 16, 2, 64, lib.PA_BF16, None) == -1
+
+
+def test_merge_validation(lib):
+    f = lib.lib.merge_attn_states
+    assert f(1, None, 1, 1, 0, 4, 2, 64, lib.PA_F32, lib.PA_BF16, None) == -1
+    assert f(1, None, 1, 1, 257, 4, 2, 64, lib.PA_F32, lib.PA_BF16, None) == -1
+    assert f(1, None, 1, 1, 2, 4, 2, 80, lib.PA_F32, lib.PA_BF16, None) == -2
+    assert f(1, None, 1, 1, 2, 4, 2, 64, 9, lib.PA_BF16, None) == -2
+    assert f(None, None, 1, 1, 2, 4, 2, 64, lib.PA_F32, lib.PA_BF16, None) == -1
+    assert f(None, None, None, None, 2, 0, 2, 64, lib.PA_F32, lib.PA_BF16, None) == 0

@@ -292,3 +292,30 @@ WORKLOADS = {
     "mixed": mixed_batch,
     "long": long_decode,
 }
+
+
+def custom(name: str, seed: int, ctx_lens, q_lens, num_heads: int, num_kv_heads: int,
+           head_size: int, block_size: int, dtype=torch.bfloat16, kind: str = "prefill",
+           window_left: int = -1, softcap: float = 0.0, alibi: bool = False,
+           num_splits: int = 1, value_mult: float = 1.0) -> Workload:
+    """A one-step workload of arbitrary shape (edge cases in tests): sequence b
+    has ctx_lens[b] cached tokens and q_lens[b] new tokens, written by
+    reshape_and_cache, then one decode (all q_lens 1) or prefill call."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    final = ctx + ql
+    nb, table = _block_table(rng, np.maximum(final, 1), block_size)
+    w = Workload(name, seed, dtype, num_heads, num_kv_heads, head_size, block_size, nb,
+                 final.astype(np.int32), ctx.astype(np.int32), table, value_mult=value_mult,
+                 scale=1.0 / math.sqrt(head_size), window_left=window_left, softcap=softcap,
+                 alibi_slopes=alibi_slopes(num_heads) if alibi else None)
+    B = len(final)
+    q = torch.cat([_query(seed, 0, b, int(ql[b]), num_heads, head_size, value_mult, dtype)
+                   for b in range(B)])
+    if kind == "decode":
+        assert (ql == 1).all()
+    w.steps.append(Step([np.arange(c, c + n) for c, n in zip(ctx, ql)], [
+        AttnCall(kind, np.arange(B), ql.astype(np.int32), final.astype(np.int32), q,
+                 num_splits=num_splits)]))
+    return w
