@@ -1,0 +1,305 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = one decode step of the batch: reshape_and_cache of the new tokens,
+split-KV paged_attn_decode, merge_attn_states.  The headline `value` is the
+decode KV-read bandwidth (algorithmic bytes: the K and V rows each query
+must see, counted once) over the whole step.  The causal prefill workload is
+measured in the same run and reported as attention TFLOP/s under "prefill".
+
+Inputs are seeded synthetic data resident in HBM before timing starts.  Each
+step uses the next of `--layers` independent caches (as consecutive layers of
+a model would) so no step re-reads K/V another step left in the caches.
+
+Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on a
+single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "decode KV-read GB/s + prefill attn TFLOP/s, bf16 paged KV, 1×MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "paged_kv_attention_29_amd", "csrc")
+
+
+def visible_keys(L: int, pos: int, causal: bool, window_left: int) -> int:
+    hi = min(L, pos + 1) if causal else L
+    lo = max(0, pos - window_left) if window_left >= 0 else 0
+    return max(0, hi - lo)
+
+
+def decode_bytes(w, call) -> int:
+    """K and V bytes every decode query must see: visible keys x Hkv x D x 2 x elem."""
+    elem = 2
+    keys = sum(visible_keys(int(L), int(L) - 1, True, w.window_left) for L in call.seq_lens)
+    return keys * w.num_kv_heads * w.head_size * 2 * elem
+
+
+def prefill_flops(w, call) -> int:
+    """4 * D * Hq per visible (query, key) pair (QK^T and PV, 2 flops per MAC)."""
+    pairs = 0
+    for nq, L in zip(call.query_lens, call.seq_lens):
+        nq, L = int(nq), int(L)
+        ctx = L - nq
+        if w.window_left < 0:
+            pairs += nq * ctx + nq * (nq + 1) // 2
+        else:
+            pairs += sum(visible_keys(L, ctx + t, True, w.window_left) for t in range(nq))
+    return 4 * w.head_size * w.num_heads * pairs
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(CSRC, n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
+    kernel source is unchanged since they were taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timed:
+    """HIP events around each launch of one kernel on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self) -> float:
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def run_decode(args, pa, runner, w):
+    call = w.steps[0].calls[0]
+    base = runner.PagedCache(w)
+    base.fill_context()
+    caches = [base]
+    for _ in range(args.layers - 1):
+        c = runner.PagedCache.__new__(runner.PagedCache)
+        c.__dict__.update(base.__dict__)
+        c.key_cache = base.key_cache.clone()
+        c.value_cache = base.value_cache.clone()
+        caches.append(c)
+    k, v, s = base.step_inputs(w.steps[0])
+    bufs = [c.call_buffers(call, args.splits) for c in caches]
+    torch.cuda.synchronize()
+
+    dec_t, rac_t, merge_t = Timed(), Timed(), Timed()
+
+    def step(i, timed):
+        c, cb = caches[i % len(caches)], bufs[i % len(caches)]
+        if timed:
+            with rac_t:
+                pa.reshape_and_cache(k, v, c.key_cache, c.value_cache, s)
+        else:
+            pa.reshape_and_cache(k, v, c.key_cache, c.value_cache, s)
+        if cb.num_splits == 1:
+            if timed:
+                with dec_t:
+                    c.run(cb)
+            else:
+                c.run(cb)
+            return
+        kw = dict(part_out=cb.part_out, part_lse=cb.part_lse)
+        if timed:
+            with dec_t:
+                pa.paged_attn_decode(None, cb.q, c.key_cache, c.value_cache, cb.seq_lens,
+                                     cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
+                                     w.softcap, c.alibi, cb.num_splits, **kw)
+            with merge_t:
+                pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
+        else:
+            pa.paged_attn_decode(None, cb.q, c.key_cache, c.value_cache, cb.seq_lens,
+                                 cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
+                                 w.softcap, c.alibi, cb.num_splits, **kw)
+            pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # whole-step wall time without the per-kernel events
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, False)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the same steps again with HIP events around each kernel
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    nbytes = decode_bytes(w, call)
+    return dict(ms_per_step=wall_ms, decode_ms=dec_t.mean_ms(), rac_ms=rac_t.mean_ms(),
+                merge_ms=merge_t.mean_ms() if merge_t.pairs else 0.0, bytes=nbytes,
+                tokens=int(s.numel()))
+
+
+def run_prefill(args, pa, runner):
+    w = W.prefill_batch()
+    call = w.steps[0].calls[0]
+    cache = runner.PagedCache(w)
+    k, v, s = cache.step_inputs(w.steps[0])
+    cb = cache.call_buffers(call)
+    pre_t, rac_t = Timed(), Timed()
+    for _ in range(args.warmup):
+        pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+        cache.run(cb)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        with rac_t:
+            pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+        with pre_t:
+            cache.run(cb)
+    torch.cuda.synchronize()
+    flops = prefill_flops(w, call)
+    ms = pre_t.mean_ms()
+    tflops = flops / (ms * 1e-3) / 1e12
+    rac_bytes = 2 * int(s.numel()) * w.num_kv_heads * w.head_size * 2 * 2
+    digest = source_digest("prefill.hip", "common.h")
+    return {
+        "value": round(tflops, 2), "unit": "TFLOP/s", "workload": w.name,
+        "ms_per_call": round(ms, 4), "flops": flops, "query_tokens": int(call.q.shape[0]),
+        "reshape_and_cache": {"ms": round(rac_t.mean_ms(), 4),
+                              "GB/s": round(rac_bytes / (rac_t.mean_ms() * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profile("prefill", digest)},
+    }
+
+
+def cpu_baseline(w, seconds: float = 10.0):
+    """The oracle (float64 PyTorch on the host) on the first sequences of the
+    same decode batch, sized to roughly `seconds` of work."""
+    import oracle
+    call = w.steps[0].calls[0]
+    threads = torch.get_num_threads()
+    done_bytes, elapsed, n = 0, 0.0, 0
+    order = list(range(call.num_seqs))
+    while elapsed < seconds and n < len(order):
+        b = order[n]
+        L = int(call.seq_lens[b])
+        nblk = -(-L // w.block_size)
+        kc = torch.full((nblk, w.block_size, w.num_kv_heads, w.head_size), float("nan"),
+                        dtype=w.dtype)
+        vc = kc.clone()
+        kk, vv = w.sequence_kv(b, 0, L)
+        pos = np.arange(L)
+        slots = torch.from_numpy((pos // w.block_size) * w.block_size + pos % w.block_size)
+        oracle.scatter(kk, vv, slots, kc, vc)
+        table = torch.arange(nblk, dtype=torch.int32)[None]
+        t0 = time.perf_counter()
+        oracle.decode(call.q[b:b + 1], kc, vc, [L], table, w.scale, w.window_left, w.softcap,
+                      w.alibi_slopes)
+        elapsed += time.perf_counter() - t0
+        done_bytes += visible_keys(L, L - 1, True, w.window_left) * w.num_kv_heads * w.head_size * 4
+        n += 1
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle decode of the first {n} of {call.num_seqs} sequences (all heads), "
+                      f"{elapsed:.1f} s of CPU time, float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "long"])
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the hot path here is single-GPU "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import paged_kv_attention_29_amd as pa
+    from paged_kv_attention_29_amd import runner
+
+    if args.workload == "decode":
+        w = W.decode_batch(num_splits=args.splits or 4)
+    elif args.workload == "mixed":
+        w = W.mixed_batch(num_splits=args.splits or 4)
+    else:
+        w = W.long_decode()
+        args.layers = 1
+    if args.splits is None:
+        args.splits = w.steps[0].calls[0].num_splits
+    call = w.steps[0].calls[0]
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    r = run_decode(args, pa, runner, w)
+    gbs = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+    kern_gbs = r["bytes"] / (r["decode_ms"] * 1e-3) / 1e9
+    digest = source_digest("decode.hip", "common.h")
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": call.num_seqs,
+                   "context_tokens": int(call.seq_lens.sum()), "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size, "num_splits": args.splits,
+                   "layers": args.layers, "step": "reshape_and_cache + decode + merge"},
+        "kernels_ms": {"reshape_and_cache": round(r["rac_ms"], 4),
+                       "paged_attn_decode": round(r["decode_ms"], 4),
+                       "merge_attn_states": round(r["merge_ms"], 4)},
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(f"decode:{w.name}:S{args.splits}", digest),
+                     "kernel": "paged_attn_decode", "bytes_per_launch": r["bytes"]},
+    }
+    if not args.no_prefill and args.workload == "decode":
+        out["prefill"] = run_prefill(args, pa, runner)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

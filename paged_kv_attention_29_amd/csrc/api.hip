@@ -135,6 +135,8 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
     return fail(PA_ERR_INVALID, "%s: NULL cu_seqlens_q", fn);
   if (num_heads / num_kv_heads > 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 128 query heads per KV head", fn);
+  if (max_seqlen_k >= (1 << 24))
+    return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
   pa::AttnParams p{};
   p.out = out;
@@ -185,6 +187,8 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
   if (num_heads / num_kv_heads > 16)
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
   if (max_seq_len < 0) return fail(PA_ERR_INVALID, "%s: max_seq_len must be >= 0", fn);
+  if (max_seq_len >= (1 << 24))
+    return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
   if (num_seqs == 0) return ok();
   pa::AttnParams p{};
   p.out = out;

@@ -14,6 +14,9 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -29,16 +32,14 @@ struct BF16 {
   static __device__ __forceinline__ float to_float(uint16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
   }
-  // round to nearest even; NaN stays NaN
+  // round to nearest even (hardware conversion); NaN stays NaN
   static __device__ __forceinline__ uint16_t from_float(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
   }
-  // two floats -> packed pair (lo in bits 0..15)
+  // two floats -> packed pair (lo in bits 0..15), one v_cvt_pk_bf16_f32
+  // (round to nearest even)
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return static_cast<uint32_t>(from_float(lo)) | (static_cast<uint32_t>(from_float(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf2));
   }
   // D[16x16] += A[16x32] * B[32x16]; operands are 8 elements per lane
   static __device__ __forceinline__ v4f mfma16x16x32(v8s a, v8s b, v4f c) {
@@ -63,8 +64,9 @@ struct F16 {
   static __device__ __forceinline__ uint16_t from_float(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
   }
+  // one v_cvt_pk_f16_f32 (round to nearest even)
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return static_cast<uint32_t>(from_float(lo)) | (static_cast<uint32_t>(from_float(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
   }
   static __device__ __forceinline__ v4f mfma16x16x32(v8s a, v8s b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
@@ -78,10 +80,6 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, a),
                                                  __builtin_bit_cast(v4h, b), c, 0, 0, 0);
   }
-};
-
-struct F32 {
-  static __device__ __forceinline__ float load(const float* p) { return *p; }
 };
 
 // ---------------------------------------------------------------------------
@@ -108,14 +106,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 // exp2 of a finite-or--inf argument (v_exp_f32); exp2(-inf) = 0
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh from exp: tanh(x) = sign(x) * (1 - 2 / (exp(2|x|) + 1)); exact limits
-// at +-inf, absolute error a few ulp of 1 near 0.
+// tanh from exp: tanh(x) = sign(x) * (1 - 2 / (exp(2|x|) + 1)) with the
+// hardware exp2 and reciprocal; exact limits at +-inf, absolute error a few
+// ulp of 1 near 0.
 __device__ __forceinline__ float tanh_f32(float x) {
   float ax = fabsf(x);
   float e = fast_exp2(2.0f * kLog2e * ax);
-  float t = 1.0f - 2.0f / (e + 1.0f);
+  float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
   return copysignf(t, x);
 }
+
+// floor(j / d) for 0 <= j < 2^24 and 16 <= d <= 256, with
+// magic = ceil(2^32 / d) computed on the host (exact in that range).
+__device__ __forceinline__ int div_magic(int j, uint32_t magic) {
+  return static_cast<int>(__umulhi(static_cast<uint32_t>(j), magic));
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j supplies the address of 4 consecutive 16-bit elements; lane i of
+// the group receives element i of the four 16-element rows those 16 pieces
+// form when laid end to end in lane order (row e = pieces of lanes 4e..4e+3).
+// So if lane j points at M[r0 + j/4][c0 + 4*(j%4)] of a row-major matrix M,
+// lane i receives M[r0 + e][c0 + i] for e = 0..3: four rows of one column.
+__device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(p));
+}
+
+// any lane of the wave
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Order LDS writes before later LDS reads of other lanes of the same wave
 // (LDS accesses of one wave are executed in order; this only stops the

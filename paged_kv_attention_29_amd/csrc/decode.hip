@@ -15,8 +15,8 @@
 //
 // K is loaded from HBM straight into the A-operand layout (16-byte pieces of
 // a key row per lane).  V needs its key index inside each lane, so each wave
-// writes its V tile to a private LDS slab row-major and reads it back
-// transposed.  The 4 waves of a workgroup take interleaved tiles of the
+// writes its V tile to a private LDS slab row-major and reads it back with
+// the LDS transpose read (one ds_read_b64_tr_b16 per PV MFMA).  The 4 waves of a workgroup take interleaved tiles of the
 // split with their own online-softmax state (fp32, base-2 exponent) and are
 // merged through LDS at the end.  The loads of the next tile are issued
 // before the current tile is computed.
@@ -41,18 +41,22 @@ struct DecodeArgs {
   const int32_t* block_table;
   int64_t bt_stride;
   int B, Hq, Hkv, G, bs, S;
+  uint32_t bs_magic;    // ceil(2^32 / bs)
   float scale_log2;     // scale * log2(e)
-  float scale;
-  float softcap;        // 0 = off
+  float scale_over_cap; // scale / softcap
+  float cap_log2;       // softcap * log2(e)
   int window_left;      // -1 = none
   const float* alibi;   // nullable
 };
 
-// LDS: per-wave V slabs of 16 rows (pitch D + 4 elements: the 8-byte pad
-// spreads the 4 rows read together over different banks), reused after the
-// key loop for the cross-wave combine: [wave][head j < G][m, l, O[0..D)].
+enum { kSoftcap = 1, kAlibi = 2 };
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+
+// LDS: per-wave V slabs of 16 rows (pitch D + 16 elements: the 32-byte pad
+// spreads the 16 rows a transpose read touches over all banks), reused after
+// the key loop for the cross-wave combine: [wave][head j < G][m, l, O[0..D)].
 template <int D>
-constexpr int kVPitch = D + 4;
+constexpr int kVPitch = D + 16;
 template <int D>
 constexpr size_t decode_lds_bytes(int G) {
   const size_t v = (size_t)kWaves * 16 * kVPitch<D> * 2;
@@ -60,8 +64,10 @@ constexpr size_t decode_lds_bytes(int G) {
   return v > c ? v : c;
 }
 
-template <typename T, int D>
+template <typename T, int D, int FEAT>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+  constexpr bool SOFTCAP = FEAT & kSoftcap;
+  constexpr bool ALIBI = FEAT & kAlibi;
   constexpr int KK = D / 32;   // QK mfma steps along D
   constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
   constexpr int P = kVPitch<D>;
@@ -89,7 +95,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 
   const int head = g * a.G + r16;  // query head of this lane's column
   const bool col_ok = r16 < a.G;
-  const float slope_log2 = (a.alibi != nullptr && col_ok) ? a.alibi[head] * kLog2e : 0.0f;
+  float slope_log2 = 0.0f;
+  if constexpr (ALIBI) slope_log2 = col_ok ? a.alibi[head] * kLog2e : 0.0f;
 
   // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8
   v8s qf[KK];
@@ -111,8 +118,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   };
   auto load_tile = [&](int tile, Frag& f) {
     const int j0 = tile << 4;
-    const int blk = btab[j0 / a.bs];
-    const int64_t slot = (int64_t)blk * a.bs + (j0 % a.bs) + r16;
+    const int q = div_magic(j0, a.bs_magic);
+    const int64_t slot = (int64_t)btab[q] * a.bs + (j0 - q * a.bs) + r16;
     const int64_t off = slot * row_stride + (int64_t)g * D + c4 * 8;
     const uint16_t* kp = a.kc + off;
     const uint16_t* vp = a.vc + off;
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     if (tn < t_end) load_tile(tn, nxt);
 
     const int j0 = tile << 4;
-    // ---- scores S^T[key j0 + 4*c4 + e][head r16]
+    // ---- scores S^T[key j0 + 4*c4 + e][head r16], in log2 units
     v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s = T::mfma16x16x32(cur.k[kk], qf[kk], s);
@@ -148,28 +155,30 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int key = j0 + 4 * c4 + e;
       float v;
-      if (a.softcap > 0.f) {
-        v = a.softcap * tanh_f32(s[e] * a.scale / a.softcap) * kLog2e;
-      } else {
-        v = s[e] * a.scale_log2;
-      }
-      v -= slope_log2 * static_cast<float>(pos - key);
+      if constexpr (SOFTCAP) v = a.cap_log2 * tanh_f32(s[e] * a.scale_over_cap);
+      else v = s[e] * a.scale_log2;
+      if constexpr (ALIBI) v -= slope_log2 * static_cast<float>(pos - key);
       x[e] = (key >= lo_vis && key < hi) ? v : kNegInf;
     }
-    // ---- online softmax over the 16 keys of this tile, per head column
+    // ---- online softmax over the 16 keys of this tile, per head column;
+    //      the reference max only moves when it grows by more than 2^8
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const bool grow = mx > m_run + kTau;
+    if (wave_any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) o[dc] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.0f : m_run;
     float pe[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(x[e] - m_use);
-    l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) o[dc] *= alpha;
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
     u32x2 pw = {T::pack2(pe[0], pe[1]), T::pack2(pe[2], pe[3])};
     const v4s pb = __builtin_bit_cast(v4s, pw);
 
@@ -182,19 +191,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-        const v8s val = row_ok ? cur.v[kk] : z;
-        u32x4 w = __builtin_bit_cast(u32x4, val);
-        *reinterpret_cast<u32x2*>(dst + kk * 32) = u32x2{w[0], w[1]};
-        *reinterpret_cast<u32x2*>(dst + kk * 32 + 4) = u32x2{w[2], w[3]};
+        *reinterpret_cast<v8s*>(dst + kk * 32) = row_ok ? cur.v[kk] : z;
       }
     }
     wave_lds_sync();
-    // ---- O^T[d][head] += V^T[d][key] P^T[key][head]
+    // ---- O^T[d][head] += V^T[d][key] P^T[key][head]; lane group c4 reads
+    //      V[4*c4 + e][dc*16 + r16] for e = 0..3 with one transpose read
+    {
+      const uint16_t* vb = vs + (4 * c4 + (r16 >> 2)) * P + 4 * (r16 & 3);
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const uint16_t* src = vs + (4 * c4) * P + dc * 16 + r16;
-      v4s av = {(short)src[0], (short)src[P], (short)src[2 * P], (short)src[3 * P]};
-      o[dc] = T::mfma16x16x16(av, pb, o[dc]);
+      for (int dc = 0; dc < DC; ++dc) o[dc] = T::mfma16x16x16(lds_read_tr16(vb + dc * 16), pb, o[dc]);
     }
     wave_lds_sync();
     cur = nxt;
@@ -248,12 +254,29 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int FEAT>
 int launch_d(const DecodeArgs& args, hipStream_t stream) {
   const int64_t grid = (int64_t)args.Hkv * args.B * args.S;
-  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((decode_kernel<T, D, FEAT>), dim3(static_cast<unsigned>(grid)),
                      dim3(kWaves * 64), decode_lds_bytes<D>(args.G), stream, args);
   return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+template <typename T, int D>
+int launch_feat(const DecodeArgs& a, bool softcap, bool alibi, hipStream_t s) {
+  if (softcap && alibi) return launch_d<T, D, kSoftcap | kAlibi>(a, s);
+  if (softcap) return launch_d<T, D, kSoftcap>(a, s);
+  if (alibi) return launch_d<T, D, kAlibi>(a, s);
+  return launch_d<T, D, 0>(a, s);
+}
+
+template <typename T>
+int launch_t(const DecodeArgs& a, int D, bool softcap, bool alibi, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_feat<T, 64>(a, softcap, alibi, s);
+    case 128: return launch_feat<T, 128>(a, softcap, alibi, s);
+    default: return launch_feat<T, 256>(a, softcap, alibi, s);
+  }
 }
 
 }  // namespace
@@ -277,17 +300,16 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.G = p.num_heads / p.num_kv_heads;
   a.bs = p.block_size;
   a.S = p.num_splits;
-  a.scale = p.scale;
+  a.bs_magic = static_cast<uint32_t>(((1ULL << 32) + p.block_size - 1) / p.block_size);
+  const bool softcap = p.softcap > 0.f;
   a.scale_log2 = p.scale * kLog2e;
-  a.softcap = p.softcap;
+  a.scale_over_cap = softcap ? p.scale / p.softcap : 0.f;
+  a.cap_log2 = p.softcap * kLog2e;
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;
-  const bool bf = p.dtype == kBF16;
-  switch (p.head_size) {
-    case 64: return bf ? launch_d<BF16, 64>(a, stream) : launch_d<F16, 64>(a, stream);
-    case 128: return bf ? launch_d<BF16, 128>(a, stream) : launch_d<F16, 128>(a, stream);
-    default: return bf ? launch_d<BF16, 256>(a, stream) : launch_d<F16, 256>(a, stream);
-  }
+  const bool alibi = p.alibi_slopes != nullptr;
+  if (p.dtype == kBF16) return launch_t<BF16>(a, p.head_size, softcap, alibi, stream);
+  return launch_t<F16>(a, p.head_size, softcap, alibi, stream);
 }
 
 }  // namespace pa

@@ -10,15 +10,24 @@
 //   O^T[D x 32 rows]      += V^T[D x 64] . P^T[64 x 32]      (mfma 32x32x16)
 // With the query row as the MFMA N index, every lane holds one query row in
 // both products, so the online-softmax row statistics are per lane (one
-// cross-lane step pairs lane l with l ^ 32), and the fp32 probabilities of
-// S^T become the B operand of the PV product in registers, without moving.
+// cross-lane step pairs lane l with l ^ 32), and the probabilities of S^T
+// become the B operand of the PV product in registers, without moving.
+//
+// Softmax work per score is kept to max, one fma, exp2, add and half a
+// packed convert: the scale is folded into the exponent, masks are applied
+// only on tiles that cut a row's visible range, tiles no row of a wave can
+// see are skipped by that wave, and the running maximum is only moved (and
+// the accumulators rescaled) when a row's maximum grows by more than 2^8
+// (the result is exact either way: numerator and denominator share the
+// same reference).
 //
 // K/V tiles are gathered block by block through the block table into
-// registers one tile ahead, then stored to a double-buffered LDS stage:
-// K row-major (16-byte rows pieces), V transposed (one LDS row per head
-// dimension) so the PV A operand is two 8-byte reads per lane.  Keys at or
-// past the sequence end are never loaded (zero in LDS), so block-table
-// padding and poisoned tails are never touched.
+// registers one tile ahead (16 consecutive lanes per 16-byte pieces of a key
+// row), then stored row-major to a double-buffered LDS stage.  The PV A
+// operand needs V with the key index inside the lane; it is read with the
+// LDS transpose read (ds_read_b64_tr_b16), two per MFMA.  Keys at or past the
+// sequence end are never loaded (zero in LDS), so block-table padding and
+// poisoned tails are never touched.
 #include "common.h"
 #include "launch.h"
 
@@ -29,6 +38,9 @@ namespace {
 constexpr int kPW = 4;      // waves per workgroup
 constexpr int kRows = 128;  // MFMA rows per workgroup
 constexpr int kKT = 64;     // keys per tile
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+
+enum { kSoftcap = 1, kAlibi = 2 };
 
 struct PrefillArgs {
   uint16_t* out;
@@ -42,27 +54,33 @@ struct PrefillArgs {
   int64_t bt_stride;
   int64_t total_q;
   int B, Hq, Hkv, G, bs, tok_per_tile;
-  float scale, scale_log2, softcap;
+  uint32_t bs_magic;
+  float scale_log2;     // scale * log2(e)
+  float scale_over_cap; // scale / softcap
+  float cap_log2;       // softcap * log2(e)
   int causal, window_left;
   const float* alibi;
 };
 
 template <int D>
-constexpr int kKPitch = D + 8;      // K rows: 16-byte pad
-constexpr int kVtPitch = kKT + 4;   // V^T rows: 8-byte pad
+constexpr int kKPitch = D + 8;      // K and V rows: 16-byte pad spreads rows over banks
 template <int D>
-constexpr int kStageBytes = (kKT * kKPitch<D> + D * kVtPitch) * 2;
+constexpr int kStageBytes = 2 * kKT * kKPitch<D> * 2;
 template <int D>
 constexpr size_t prefill_lds_bytes() { return 2 * (size_t)kStageBytes<D>; }
+template <int D>
+constexpr int kMinBlocks = D <= 128 ? 2 : 1;
 
-template <typename T, int D>
-__global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
+template <typename T, int D, int FEAT>
+__global__ __launch_bounds__(kPW * 64, kMinBlocks<D>) void prefill_kernel(PrefillArgs a) {
+  constexpr bool SOFTCAP = FEAT & kSoftcap;
+  constexpr bool ALIBI = FEAT & kAlibi;
   constexpr int KQ = D / 16;        // QK mfma steps along D
   constexpr int DC = D / 32;        // PV output chunks of 32 head dims
   constexpr int V8 = D / 8;         // 16-byte pieces per row
+  constexpr int V8_SHIFT = D == 64 ? 3 : (D == 128 ? 4 : 5);
   constexpr int LPT = kKT * V8 / (kPW * 64);  // pieces per thread per tile (K and V each)
   constexpr int KP = kKPitch<D>;
-  constexpr int VP = kVtPitch;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -80,9 +98,9 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
   if (tok0 >= nq) return;
   const int L = a.seq_lens[b];
   const int ctx = L - nq;
-  const int tok_end = min(nq, tok0 + a.tok_per_tile);
+  const int ntok = min(nq - tok0, a.tok_per_tile);
   const int p_first = ctx + tok0;
-  const int p_last = ctx + tok_end - 1;
+  const int p_last = p_first + ntok - 1;
   const int k_hi = a.causal ? min(L, p_last + 1) : L;
   const int k_lo = a.window_left >= 0 ? max(0, p_first - a.window_left) : 0;
   const int t_begin = k_lo / kKT;
@@ -92,10 +110,17 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
   const int row = wave * 32 + r32;
   const int tk = row / a.G;
   const int hh = row - tk * a.G;
-  const bool row_ok = row < a.tok_per_tile * a.G && tok0 + tk < nq;
+  const bool row_ok = tk < ntok;
   const int pos = ctx + tok0 + tk;
   const int head = g * a.G + hh;
-  const float slope_log2 = (a.alibi != nullptr && row_ok) ? a.alibi[head] * kLog2e : 0.0f;
+  // positions of this wave's first and last valid rows (wave-uniform)
+  const int w_tk0 = (wave * 32) / a.G;
+  const int w_tk1 = min((wave * 32 + 31) / a.G, ntok - 1);
+  const bool w_rows = w_tk0 < ntok;
+  const int w_pmin = ctx + tok0 + w_tk0;
+  const int w_pmax = ctx + tok0 + w_tk1;
+  float slope_log2 = 0.0f;
+  if constexpr (ALIBI) slope_log2 = row_ok ? a.alibi[head] * kLog2e : 0.0f;
 
   v8s qf[KQ];
   {
@@ -109,59 +134,54 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
 
   const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const int64_t head_off = (int64_t)g * D;
+  const uint16_t* kc = a.kc + (int64_t)g * D;
+  const uint16_t* vc = a.vc + (int64_t)g * D;
+  auto slot_of = [&](int j) -> int64_t {
+    const int q = div_magic(j, a.bs_magic);
+    return (int64_t)btab[q] * a.bs + (j - q * a.bs);
+  };
 
   // ---- tile loads into registers
   v8s kreg[LPT], vreg[LPT];
   auto load_tile = [&](int tile) {
     const int kbase = tile * kKT;
+    const bool full = kbase + kKT <= L;
+    const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int v = i * kPW * 64 + tid;
-      const int key = v / V8;
-      const int d8 = v - key * V8;
-      const int j = kbase + key;
-      v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-      kreg[i] = z;
-      if (j < L) {
-        const int64_t slot = (int64_t)btab[j / a.bs] * a.bs + (j % a.bs);
-        kreg[i] = *reinterpret_cast<const v8s*>(a.kc + slot * row_stride + head_off + d8 * 8);
-      }
+      const int j = kbase + (v >> V8_SHIFT);
+      const int d8 = v & (V8 - 1);
+      if (full || j < L)
+        kreg[i] = *reinterpret_cast<const v8s*>(kc + slot_of(j) * row_stride + d8 * 8);
+      else
+        kreg[i] = z;
     }
-    {
-      const int key = tid % kKT;
-      const int j = kbase + key;
-      int64_t base = -1;
-      if (j < L) base = ((int64_t)btab[j / a.bs] * a.bs + (j % a.bs)) * row_stride + head_off;
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int d8 = tid / kKT + (kPW * 64 / kKT) * i;
-        v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-        vreg[i] = base >= 0 ? *reinterpret_cast<const v8s*>(a.vc + base + d8 * 8) : z;
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int v = i * kPW * 64 + tid;
+      const int j = kbase + (v >> V8_SHIFT);
+      const int d8 = v & (V8 - 1);
+      if (full || j < L)
+        vreg[i] = *reinterpret_cast<const v8s*>(vc + slot_of(j) * row_stride + d8 * 8);
+      else
+        vreg[i] = z;
     }
   };
   auto store_tile = [&](int stage) {
     uint16_t* ks = reinterpret_cast<uint16_t*>(smem + stage * kStageBytes<D>);
-    uint16_t* vt = ks + kKT * KP;
+    uint16_t* vs = ks + kKT * KP;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int v = i * kPW * 64 + tid;
-      const int key = v / V8;
-      const int d8 = v - key * V8;
-      *reinterpret_cast<v8s*>(ks + key * KP + d8 * 8) = kreg[i];
-    }
-    const int key = tid % kKT;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int d8 = tid / kKT + (kPW * 64 / kKT) * i;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(d8 * 8 + e) * VP + key] = static_cast<uint16_t>(vreg[i][e]);
+      const int off = (v >> V8_SHIFT) * KP + (v & (V8 - 1)) * 8;
+      *reinterpret_cast<v8s*>(ks + off) = kreg[i];
+      *reinterpret_cast<v8s*>(vs + off) = vreg[i];
     }
   };
 
-  float m_run = kNegInf;
-  float l_run = 0.0f;
+  float m_run = kNegInf;   // reference maximum of the row (log2 units)
+  float l_run = 0.0f;      // this lane's half of the row sum
   v16f oacc[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc)
@@ -174,83 +194,113 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
+  // logits z: raw score (no softcap / ALiBi) scaled by cz in the exponent, or
+  // the finished log2-unit logit with cz = 1
+  const float cz = (SOFTCAP || ALIBI) ? 1.0f : a.scale_log2;
+
   for (int tile = t_begin; tile < t_end; ++tile) {
     const int stage = (tile - t_begin) & 1;
     const bool more = tile + 1 < t_end;
     if (more) load_tile(tile + 1);
 
-    const uint16_t* ks = reinterpret_cast<const uint16_t*>(smem + stage * kStageBytes<D>);
-    const uint16_t* vt = ks + kKT * KP;
     const int kbase = tile * kKT;
+    bool active = w_rows;
+    if (a.causal) active = active && kbase <= w_pmax;
+    if (a.window_left >= 0) active = active && kbase + kKT - 1 >= w_pmin - a.window_left;
 
-    // ---- S^T = K Q^T for keys kbase + [0, 32) and [32, 64)
-    v16f sacc[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
-      const uint16_t* krow = ks + (h2 * 32 + r32) * KP + 8 * g2;
-#pragma unroll
-      for (int kk = 0; kk < KQ; ++kk)
-        sacc[h2] = T::mfma32x32x16(*reinterpret_cast<const v8s*>(krow + 16 * kk), qf[kk], sacc[h2]);
-    }
+    if (active) {
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(smem + stage * kStageBytes<D>);
+      const uint16_t* vs = ks + kKT * KP;
 
-    // ---- scores -> base-2 logits with masks; lane holds keys
-    //      kbase + 32*h2 + 8*(e/4) + 4*g2 + e%4 of its row
-    float x[2][16];
-    float mx = kNegInf;
+      // ---- S^T = K Q^T for keys kbase + [0, 32) and [32, 64)
+      v16f sacc[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-        float v;
-        if (a.softcap > 0.f)
-          v = a.softcap * tanh_f32(sacc[h2][e] * a.scale / a.softcap) * kLog2e;
-        else
-          v = sacc[h2][e] * a.scale_log2;
-        const int dist = pos - key;
-        v -= slope_log2 * static_cast<float>(dist < 0 ? -dist : dist);
-        bool vis = key < L;
-        if (a.causal) vis = vis && key <= pos;
-        if (a.window_left >= 0) vis = vis && key >= pos - a.window_left;
-        v = vis ? v : kNegInf;
-        x[h2][e] = v;
-        mx = fmaxf(mx, v);
+        for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
+        const uint16_t* krow = ks + (h2 * 32 + r32) * KP + 8 * g2;
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk)
+          sacc[h2] = T::mfma32x32x16(*reinterpret_cast<const v8s*>(krow + 16 * kk), qf[kk],
+                                     sacc[h2]);
       }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.0f;
-    v8s pb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = fast_exp2(x[s >> 1][8 * (s & 1) + e] - m_use);
-        psum += pv[e];
-      }
-      u32x4 w = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
-                 T::pack2(pv[6], pv[7])};
-      pb[s] = __builtin_bit_cast(v8s, w);
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
 
-    // ---- O^T += V^T P^T; keys of step s: 16s + 4*g2 + [0,4) and 16s + 8 + 4*g2 + [0,4)
+      // ---- logits; lane holds keys kbase + 32*h2 + 8*(e/4) + 4*g2 + e%4 of its row
+      const bool need_mask = kbase + kKT > L || (a.causal && kbase + kKT - 1 > w_pmin) ||
+                             (a.window_left >= 0 && kbase < w_pmax - a.window_left);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const uint16_t* vrow = vt + (dc * 32 + r32) * VP + 16 * s + 4 * g2;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[dc] = T::mfma32x32x16(__builtin_bit_cast(v8s, w), pb[s], oacc[dc]);
+        for (int e = 0; e < 16; ++e) {
+          float z = sacc[h2][e];
+          const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+          if constexpr (SOFTCAP) z = a.cap_log2 * tanh_f32(z * a.scale_over_cap);
+          else if constexpr (ALIBI) z = z * a.scale_log2;
+          if constexpr (ALIBI) z -= slope_log2 * static_cast<float>(abs(pos - key));
+          sacc[h2][e] = z;
+        }
+      if (need_mask) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+            bool vis = key < L;
+            if (a.causal) vis = vis && key <= pos;
+            if (a.window_left >= 0) vis = vis && key >= pos - a.window_left;
+            sacc[h2][e] = vis ? sacc[h2][e] : kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_tile = mx * cz;
+
+      // ---- lazy rescale: move the reference only when the max grew a lot
+      const bool grow = m_tile > m_run + kTau;
+      if (wave_any(grow)) {
+        const float m_new = grow ? m_tile : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == kNegInf ? 0.0f : -m_run;
+
+      float psum = 0.0f;
+      v8s pb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], cz, neg_m));
+          psum += pv[e];
+        }
+        u32x4 w = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
+                   T::pack2(pv[6], pv[7])};
+        pb[s] = __builtin_bit_cast(v8s, w);
+      }
+      l_run += psum;
+
+      // ---- O^T += V^T P^T; the A operand of step s holds V[16s + 4*g2 + [0,4)][d] and
+      //      V[16s + 8 + 4*g2 + [0,4)][d] for d = dc*32 + r32 (two transpose reads)
+      const uint16_t* vbase = vs + (4 * g2 + ((lane & 15) >> 2)) * KP + 16 * ((lane >> 4) & 1) +
+                              4 * (lane & 3);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const uint16_t* p0 = vbase + (16 * s) * KP + dc * 32;
+          const v4s lo = lds_read_tr16(p0);
+          const v4s hi = lds_read_tr16(p0 + 8 * KP);
+          const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dc] = T::mfma32x32x16(av, pb[s], oacc[dc]);
+        }
       }
     }
 
@@ -261,7 +311,7 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
   const float l_tot = l_run + shfl_xor(l_run, 32);
   if (!row_ok) return;
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.0f;
+  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
   const int64_t qrow = q0 + tok0 + tk;
   uint16_t* orow = a.out + (qrow * a.Hq + head) * D + 4 * g2;
 #pragma unroll
@@ -274,26 +324,40 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x2*>(orow + dc * 32 + 8 * e4) = w;
     }
   if (a.lse != nullptr && g2 == 0)
-    a.lse[(int64_t)head * a.total_q + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+    a.lse[(int64_t)head * a.total_q + qrow] =
+        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
 }
 
-template <typename T, int D>
+template <typename T, int D, int FEAT>
 int launch_p(const PrefillArgs& args, int max_seqlen_q, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D, FEAT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   static_cast<int>(prefill_lds_bytes<D>())) == hipSuccess;
+  }
   const int ntiles = (max_seqlen_q + args.tok_per_tile - 1) / args.tok_per_tile;
   if (ntiles == 0) return 0;
   const dim3 grid(args.Hkv, args.B, ntiles);
-  hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kPW * 64), prefill_lds_bytes<D>(), stream,
-                     args);
+  hipLaunchKernelGGL((prefill_kernel<T, D, FEAT>), grid, dim3(kPW * 64), prefill_lds_bytes<D>(),
+                     stream, args);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 template <typename T, int D>
-void set_lds_limit() {
-  static bool done = false;
-  if (!done) {
-    done = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(prefill_lds_bytes<D>())) == hipSuccess;
+int launch_feat(const PrefillArgs& a, int mq, bool softcap, bool alibi, hipStream_t s) {
+  if (softcap && alibi) return launch_p<T, D, kSoftcap | kAlibi>(a, mq, s);
+  if (softcap) return launch_p<T, D, kSoftcap>(a, mq, s);
+  if (alibi) return launch_p<T, D, kAlibi>(a, mq, s);
+  return launch_p<T, D, 0>(a, mq, s);
+}
+
+template <typename T>
+int launch_t(const PrefillArgs& a, int D, int mq, bool softcap, bool alibi, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_feat<T, 64>(a, mq, softcap, alibi, s);
+    case 128: return launch_feat<T, 128>(a, mq, softcap, alibi, s);
+    default: return launch_feat<T, 256>(a, mq, softcap, alibi, s);
   }
 }
 
@@ -317,28 +381,18 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.Hkv = p.num_kv_heads;
   a.G = p.num_heads / p.num_kv_heads;
   a.bs = p.block_size;
+  a.bs_magic = static_cast<uint32_t>(((1ULL << 32) + p.block_size - 1) / p.block_size);
   a.tok_per_tile = kRows / a.G;
-  a.scale = p.scale;
+  const bool softcap = p.softcap > 0.f;
   a.scale_log2 = p.scale * kLog2e;
-  a.softcap = p.softcap;
+  a.scale_over_cap = softcap ? p.scale / p.softcap : 0.f;
+  a.cap_log2 = p.softcap * kLog2e;
   a.causal = p.causal;
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;
-  const bool bf = p.dtype == kBF16;
-  switch (p.head_size) {
-    case 64:
-      if (bf) { set_lds_limit<BF16, 64>(); return launch_p<BF16, 64>(a, p.max_seqlen_q, stream); }
-      set_lds_limit<F16, 64>();
-      return launch_p<F16, 64>(a, p.max_seqlen_q, stream);
-    case 128:
-      if (bf) { set_lds_limit<BF16, 128>(); return launch_p<BF16, 128>(a, p.max_seqlen_q, stream); }
-      set_lds_limit<F16, 128>();
-      return launch_p<F16, 128>(a, p.max_seqlen_q, stream);
-    default:
-      if (bf) { set_lds_limit<BF16, 256>(); return launch_p<BF16, 256>(a, p.max_seqlen_q, stream); }
-      set_lds_limit<F16, 256>();
-      return launch_p<F16, 256>(a, p.max_seqlen_q, stream);
-  }
+  const bool alibi = p.alibi_slopes != nullptr;
+  if (p.dtype == kBF16) return launch_t<BF16>(a, p.head_size, p.max_seqlen_q, softcap, alibi, stream);
+  return launch_t<F16>(a, p.head_size, p.max_seqlen_q, softcap, alibi, stream);
 }
 
 }  // namespace pa
