@@ -52,29 +52,39 @@ struct DecodeArgs {
 enum { kSoftcap = 1, kAlibi = 2 };
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// LDS: per-wave V slabs of 16 rows (pitch D + 16 elements: the 32-byte pad
-// spreads the 16 rows a transpose read touches over all banks), reused after
-// the key loop for the cross-wave combine: [wave][head j < G][m, l, O[0..D)].
+// Keys per iteration: NT MFMA row tiles of 16 (two for D <= 128, so a wave
+// keeps 16 KB of K/V in flight while it computes the previous 32 keys).
+template <int D>
+constexpr int kNT = D <= 128 ? 2 : 1;
+
+// LDS: per-wave V slabs of 16 * NT rows (pitch D + 16 elements: the 32-byte
+// pad spreads the 16 rows a transpose read touches over all banks), reused
+// after the key loop for the cross-wave combine: [wave][head j < G][m, l, O].
 template <int D>
 constexpr int kVPitch = D + 16;
 template <int D>
 constexpr size_t decode_lds_bytes(int G) {
-  const size_t v = (size_t)kWaves * 16 * kVPitch<D> * 2;
+  const size_t v = (size_t)kWaves * 16 * kNT<D> * kVPitch<D> * 2;
   const size_t c = (size_t)kWaves * G * (D + 2) * 4;
   return v > c ? v : c;
 }
 
+template <int D>
+constexpr int kMinBlocks = D <= 128 ? 2 : 1;
+
 template <typename T, int D, int FEAT>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(DecodeArgs a) {
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
   constexpr int KK = D / 32;   // QK mfma steps along D
   constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
+  constexpr int NT = kNT<D>;
+  constexpr int KPS = 16 * NT; // keys per step
   constexpr int P = kVPitch<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;   // key row of the K piece / head column of the tile
   const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
 
@@ -90,8 +100,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int lo = min(split * chunk, L);
   const int hi = min(lo + chunk, L);
   const int lo_vis = a.window_left >= 0 ? max(lo, pos - a.window_left) : lo;
-  const int t_begin = lo_vis >> 4;
-  const int t_end = (hi + 15) >> 4;
+  const int s_begin = lo_vis / KPS;
+  const int s_end = (hi + KPS - 1) / KPS;
 
   const int head = g * a.G + r16;  // query head of this lane's column
   const bool col_ok = r16 < a.G;
@@ -111,58 +121,72 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 
   const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive slots
+  const uint16_t* kcg = a.kc + (int64_t)g * D + c4 * 8;
+  const uint16_t* vcg = a.vc + (int64_t)g * D + c4 * 8;
 
   struct Frag {
-    v8s k[KK];
-    v8s v[KK];
+    v8s k[NT][KK];
+    v8s v[NT][KK];
   };
-  auto load_tile = [&](int tile, Frag& f) {
-    const int j0 = tile << 4;
-    const int q = div_magic(j0, a.bs_magic);
-    const int64_t slot = (int64_t)btab[q] * a.bs + (j0 - q * a.bs) + r16;
-    const int64_t off = slot * row_stride + (int64_t)g * D + c4 * 8;
-    const uint16_t* kp = a.kc + off;
-    const uint16_t* vp = a.vc + off;
+  // Block ids of a step's tiles.  Loads are branch-free (so the compiler can
+  // count outstanding loads exactly): a tile starting at or past hi is
+  // clamped to the split's last tile, loaded, and fully masked.  The clamped
+  // tile starts before hi, so it lies inside the sequence's last used block
+  // at worst (block_size is a multiple of 16) and its block-table entry is
+  // valid.
+  const int last_j0 = hi > 0 ? ((hi - 1) & ~15) : 0;
+  auto tile_j0 = [&](int step, int nt) { return min(step * KPS + 16 * nt, last_j0); };
+  auto fetch_ids = [&](int step, int (&ids)[NT]) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      f.k[kk] = *reinterpret_cast<const v8s*>(kp + kk * 32);
-      f.v[kk] = *reinterpret_cast<const v8s*>(vp + kk * 32);
+    for (int nt = 0; nt < NT; ++nt) ids[nt] = btab[div_magic(tile_j0(step, nt), a.bs_magic)];
+  };
+  auto load_step = [&](int step, const int (&ids)[NT], Frag& f) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int j0 = tile_j0(step, nt);
+      const int q = div_magic(j0, a.bs_magic);
+      const int64_t slot = (int64_t)ids[nt] * a.bs + (j0 - q * a.bs) + r16;
+      const uint16_t* kp = kcg + slot * row_stride;
+      const uint16_t* vp = vcg + slot * row_stride;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        f.k[nt][kk] = *reinterpret_cast<const v8s*>(kp + kk * 32);
+        f.v[nt][kk] = *reinterpret_cast<const v8s*>(vp + kk * 32);
+      }
     }
   };
 
-  float m_run = kNegInf;  // running max (base-2 units) of column r16
+  float m_run = kNegInf;  // reference max (log2 units) of column r16
   float l_run = 0.0f;     // this lane's share of the running sum
   v4f o[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) o[dc] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * 16 * P;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * KPS * P;
 
-  Frag cur, nxt;
-  int tile = t_begin + wave;
-  if (tile < t_end) load_tile(tile, cur);
-  for (; tile < t_end; tile += kWaves) {
-    const int tn = tile + kWaves;
-    if (tn < t_end) load_tile(tn, nxt);
-
-    const int j0 = tile << 4;
-    // ---- scores S^T[key j0 + 4*c4 + e][head r16], in log2 units
-    v4f s = {0.f, 0.f, 0.f, 0.f};
+  auto compute_step = [&](int step, const Frag& f) {
+    float x[NT][4];
+    float mx = kNegInf;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = T::mfma16x16x32(cur.k[kk], qf[kk], s);
-    float x[4];
+    for (int nt = 0; nt < NT; ++nt) {
+      const int j0 = step * KPS + 16 * nt;
+      // ---- scores S^T[key j0 + 4*c4 + e][head r16], in log2 units
+      v4f sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = j0 + 4 * c4 + e;
-      float v;
-      if constexpr (SOFTCAP) v = a.cap_log2 * tanh_f32(s[e] * a.scale_over_cap);
-      else v = s[e] * a.scale_log2;
-      if constexpr (ALIBI) v -= slope_log2 * static_cast<float>(pos - key);
-      x[e] = (key >= lo_vis && key < hi) ? v : kNegInf;
+      for (int kk = 0; kk < KK; ++kk) sc = T::mfma16x16x32(f.k[nt][kk], qf[kk], sc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = j0 + 4 * c4 + e;
+        float v;
+        if constexpr (SOFTCAP) v = a.cap_log2 * tanh_f32(sc[e] * a.scale_over_cap);
+        else v = sc[e] * a.scale_log2;
+        if constexpr (ALIBI) v -= slope_log2 * static_cast<float>(pos - key);
+        x[nt][e] = (key >= lo_vis && key < hi) ? v : kNegInf;
+        mx = fmaxf(mx, x[nt][e]);
+      }
     }
-    // ---- online softmax over the 16 keys of this tile, per head column;
-    //      the reference max only moves when it grows by more than 2^8
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    // ---- online softmax per head column; the reference max only moves when
+    //      it grows by more than 2^8
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const bool grow = mx > m_run + kTau;
@@ -175,34 +199,78 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.0f : m_run;
-    float pe[4];
+    // P^T as the PV B operand: lane (head r16, quarter c4) holds keys
+    // 16*nt + 4*c4 + e of each tile; with two tiles they form one 8-element
+    // operand of a 16x16x32 MFMA (key slots 4*c4 + e and 16 + 4*c4 + e)
+    uint32_t pw[2 * NT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(x[e] - m_use);
-    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    u32x2 pw = {T::pack2(pe[0], pe[1]), T::pack2(pe[2], pe[3])};
-    const v4s pb = __builtin_bit_cast(v4s, pw);
-
-    // ---- V tile -> LDS (row r16); rows outside [lo_vis, hi) become zero so
-    //      stale or poisoned cache contents never reach the accumulator
-    {
-      const int key = j0 + r16;
+    for (int nt = 0; nt < NT; ++nt) {
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(x[nt][e] - m_use);
+      l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+      pw[2 * nt] = T::pack2(pe[0], pe[1]);
+      pw[2 * nt + 1] = T::pack2(pe[2], pe[3]);
+    }
+    // ---- V -> LDS rows 16*nt + r16; rows outside [lo_vis, hi) become zero
+    //      so stale or poisoned cache contents never reach the accumulator
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int key = step * KPS + 16 * nt + r16;
       const bool row_ok = key >= lo_vis && key < hi;
-      uint16_t* dst = vs + r16 * P + c4 * 8;
+      uint16_t* dst = vs + (16 * nt + r16) * P + c4 * 8;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-        *reinterpret_cast<v8s*>(dst + kk * 32) = row_ok ? cur.v[kk] : z;
+        const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+        *reinterpret_cast<v8s*>(dst + kk * 32) = row_ok ? f.v[nt][kk] : z;
       }
     }
     wave_lds_sync();
     // ---- O^T[d][head] += V^T[d][key] P^T[key][head]; lane group c4 reads
-    //      V[4*c4 + e][dc*16 + r16] for e = 0..3 with one transpose read
-    {
-      const uint16_t* vb = vs + (4 * c4 + (r16 >> 2)) * P + 4 * (r16 & 3);
+    //      V[16*nt + 4*c4 + e][dc*16 + r16] for e = 0..3 with one transpose
+    //      read per tile
+    const uint16_t* vb = vs + (4 * c4 + (r16 >> 2)) * P + 4 * (r16 & 3);
+    if constexpr (NT == 2) {
+      const u32x4 pq = {pw[0], pw[1], pw[2], pw[3]};
+      const v8s pb = __builtin_bit_cast(v8s, pq);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const v4s lo = lds_read_tr16(vb + dc * 16);
+        const v4s hi = lds_read_tr16(vb + 16 * P + dc * 16);
+        const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dc] = T::mfma16x16x32(av, pb, o[dc]);
+      }
+    } else {
+      const u32x2 pq = {pw[0], pw[1]};
+      const v4s pb = __builtin_bit_cast(v4s, pq);
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) o[dc] = T::mfma16x16x16(lds_read_tr16(vb + dc * 16), pb, o[dc]);
     }
     wave_lds_sync();
+  };
+
+  // ---- double buffer: the next step's loads are in flight while the
+  //      current one is computed.  Block ids run one step further ahead and
+  //      are issued before the K/V loads, so waiting for them never waits for
+  //      K/V data (the vector-memory counter completes in issue order).
+  Frag cur, nxt;
+  int ids[NT];
+  int step = s_begin + wave;
+  if (step < s_end) {
+    fetch_ids(step, ids);
+    load_step(step, ids, cur);
+    fetch_ids(min(step + kWaves, s_end - 1), ids);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first step landed
+  for (; step < s_end; step += kWaves) {
+    if (step + kWaves < s_end) {
+      int ids2[NT];
+      fetch_ids(min(step + 2 * kWaves, s_end - 1), ids2);
+      load_step(step + kWaves, ids, nxt);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) ids[nt] = ids2[nt];
+    }
+    compute_step(step, cur);
     cur = nxt;
   }
 
@@ -236,9 +304,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float* row = comb + (w * a.G + j) * CP;
-        const float f = fast_exp2(row[0] - M);
-        den += f * row[1];
-        num += f * row[2 + d];
+        const float fw = fast_exp2(row[0] - M);
+        den += fw * row[1];
+        num += fw * row[2 + d];
       }
     }
     const float val = den > 0.f ? num / den : 0.f;

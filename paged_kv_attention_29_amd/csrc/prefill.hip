@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kPW * 64, kMinBlocks<D>) void prefill_kernel(Prefil
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31;
   const int g2 = lane >> 5;
 
@@ -121,6 +121,10 @@ __global__ __launch_bounds__(kPW * 64, kMinBlocks<D>) void prefill_kernel(Prefil
   const int w_pmax = ctx + tok0 + w_tk1;
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = row_ok ? a.alibi[head] * kLog2e : 0.0f;
+  // keys visible to this row: lo_row <= key <= hi_row
+  const int hi_row = a.causal ? min(pos, L - 1) : L - 1;
+  const int lo_row = a.window_left >= 0 ? max(pos - a.window_left, 0) : 0;
+  const uint32_t span_row = static_cast<uint32_t>(hi_row - lo_row);
 
   v8s qf[KQ];
   {
@@ -141,31 +145,43 @@ __global__ __launch_bounds__(kPW * 64, kMinBlocks<D>) void prefill_kernel(Prefil
     return (int64_t)btab[q] * a.bs + (j - q * a.bs);
   };
 
-  // ---- tile loads into registers
+  // ---- tile loads into registers: piece v = i * 256 + tid of the tile is key
+  //      v / V8, head-dim piece v % V8; K and V share the slot arithmetic
+  constexpr int KPI = kPW * 64 / V8;  // keys covered by one i
   v8s kreg[LPT], vreg[LPT];
   auto load_tile = [&](int tile) {
     const int kbase = tile * kKT;
-    const bool full = kbase + kKT <= L;
-    const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int d8 = tid & (V8 - 1);
+    const int kl = tid >> V8_SHIFT;
+    if (kbase + kKT <= L) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int v = i * kPW * 64 + tid;
-      const int j = kbase + (v >> V8_SHIFT);
-      const int d8 = v & (V8 - 1);
-      if (full || j < L)
-        kreg[i] = *reinterpret_cast<const v8s*>(kc + slot_of(j) * row_stride + d8 * 8);
-      else
+      for (int i = 0; i < LPT; ++i) {
+        int64_t slot;
+        if constexpr (KPI <= 16) {
+          // the KPI keys of step i lie in one cache block: uniform block id
+          const int j0 = kbase + i * KPI;
+          const int q = div_magic(j0, a.bs_magic);
+          slot = (int64_t)btab[q] * a.bs + (j0 - q * a.bs) + kl;
+        } else {
+          slot = slot_of(kbase + i * KPI + kl);
+        }
+        const int64_t off = slot * row_stride + d8 * 8;
+        kreg[i] = *reinterpret_cast<const v8s*>(kc + off);
+        vreg[i] = *reinterpret_cast<const v8s*>(vc + off);
+      }
+    } else {
+      const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int j = kbase + i * KPI + kl;
         kreg[i] = z;
-    }
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int v = i * kPW * 64 + tid;
-      const int j = kbase + (v >> V8_SHIFT);
-      const int d8 = v & (V8 - 1);
-      if (full || j < L)
-        vreg[i] = *reinterpret_cast<const v8s*>(vc + slot_of(j) * row_stride + d8 * 8);
-      else
         vreg[i] = z;
+        if (j < L) {
+          const int64_t off = slot_of(j) * row_stride + d8 * 8;
+          kreg[i] = *reinterpret_cast<const v8s*>(kc + off);
+          vreg[i] = *reinterpret_cast<const v8s*>(vc + off);
+        }
+      }
     }
   };
   auto store_tile = [&](int stage) {
@@ -192,6 +208,9 @@ __global__ __launch_bounds__(kPW * 64, kMinBlocks<D>) void prefill_kernel(Prefil
     load_tile(t_begin);
     store_tile(0);
   }
+  // every global load so far (Q included) has landed: keeps the compiler
+  // from waiting on the next-tile prefetch at the first use of Q in the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   // logits z: raw score (no softcap / ALiBi) scaled by cz in the exponent, or
@@ -240,15 +259,14 @@ __global__ __launch_bounds__(kPW * 64, kMinBlocks<D>) void prefill_kernel(Prefil
           sacc[h2][e] = z;
         }
       if (need_mask) {
+        // visible iff 0 <= key - lo_row <= span_row (unsigned compare)
+        const int base = kbase + 4 * g2 - lo_row;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-            bool vis = key < L;
-            if (a.causal) vis = vis && key <= pos;
-            if (a.window_left >= 0) vis = vis && key >= pos - a.window_left;
-            sacc[h2][e] = vis ? sacc[h2][e] : kNegInf;
+            const uint32_t rel = static_cast<uint32_t>(base + 32 * h2 + 8 * (e >> 2) + (e & 3));
+            sacc[h2][e] = rel <= span_row ? sacc[h2][e] : kNegInf;
           }
       }
       float mx = kNegInf;

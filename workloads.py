@@ -217,7 +217,7 @@ def _decode_workload(name, seed, lens, Hq, Hkv, D, bs, num_splits, dtype=torch.b
     return w
 
 
-def decode_batch(seed: int = 2, num_splits: int = 4) -> Workload:
+def decode_batch(seed: int = 2, num_splits: int = 8) -> Workload:
     """bf16 decode: 64 sequences, context uniform in [512, 4096], 32 query /
     8 KV heads of size 128, block 16, shuffled pool sized for the context
     plus 10%, no masks."""
