@@ -254,9 +254,9 @@ def main():
     from paged_kv_attention_29_amd import runner
 
     if args.workload == "decode":
-        w = W.decode_batch(num_splits=args.splits or 4)
+        w = W.decode_batch() if args.splits is None else W.decode_batch(num_splits=args.splits)
     elif args.workload == "mixed":
-        w = W.mixed_batch(num_splits=args.splits or 4)
+        w = W.mixed_batch() if args.splits is None else W.mixed_batch(num_splits=args.splits)
     else:
         w = W.long_decode()
         args.layers = 1
