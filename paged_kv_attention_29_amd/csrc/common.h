@@ -41,6 +41,11 @@ struct BF16 {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf2));
   }
+  // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 with (1, 1))
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pair),
+                                           __builtin_bit_cast(bf2, 0x3f803f80u), acc, false);
+  }
   // D[16x16] += A[16x32] * B[32x16]; operands are 8 elements per lane
   static __device__ __forceinline__ v4f mfma16x16x32(v8s a, v8s b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
@@ -67,6 +72,10 @@ struct F16 {
   // one v_cvt_pk_f16_f32 (round to nearest even)
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pair), __builtin_bit_cast(h2, 0x3c003c00u),
+                                  acc, false);
   }
   static __device__ __forceinline__ v4f mfma16x16x32(v8s a, v8s b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
