@@ -37,7 +37,7 @@
 #include "common.h"
 #include "launch.h"
 
-#include <type_traits>
+#include <type_traits>  // std::true_type
 
 namespace pa {
 
@@ -47,6 +47,9 @@ constexpr int kKT = 64;       // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
 enum { kSoftcap = 1, kAlibi = 2 };
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 struct PrefillArgs {
   uint16_t* out;
@@ -68,10 +71,15 @@ struct PrefillArgs {
   const float* alibi;
 };
 
+// Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
+// several workgroups share a CU (two for D = 128, three for D = 64): one
+// workgroup's Q loads and output stores overlap another's tiles.
 template <int D>
-constexpr int kNW = D <= 128 ? 8 : 4;  // waves per workgroup (2 per SIMD / 1 per SIMD)
+constexpr int kNW = 4;  // waves per workgroup
 template <int D>
-constexpr int kNST = D <= 128 ? 3 : 2;  // LDS ring stages
+constexpr int kNST = 2;  // LDS ring stages
+template <int D>
+constexpr int kMinWG = D == 64 ? 3 : D == 128 ? 2 : 1;  // workgroups per CU
 template <int D>
 constexpr int kRows = 32 * kNW<D>;     // MFMA rows per workgroup
 template <int D>
@@ -97,46 +105,51 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
 }
 
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
-                                   0);
+// 16 bytes per lane from sbase + voff (global memory) into LDS at byte
+// address lds_base + 16 * lane (global_load_lds_dwordx4; sbase and lds_base
+// wave-uniform).  Issued as asm: a DMA the compiler knows of makes it wait
+// for every LDS DMA in flight before each later LDS read, since it cannot
+// tell the stages apart, which would empty the ring.  The DMA waits are
+// placed by hand instead (wait_vmcnt before the hand-off barrier).  M0,
+// which holds the LDS base, is restored afterwards.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_base), "v"(voff), "s"(sbase));
 }
 
-// Workgroup barrier for LDS hand-off.  __syncthreads() would make the
-// compiler wait for every LDS DMA in flight (vmcnt(0)), which empties the
-// ring; the DMA waits are placed explicitly instead, and this barrier only
-// drains this wave's LDS reads.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// ds_read_b64_tr_b16 (see lds_read_tr16) at byte address addr + OFF.  Issued
-// as asm so the compiler does not wait for the LDS DMA in flight before it
-// (it cannot tell that the DMA writes another stage); the result must be
-// claimed with lgkm_claim after the matching lgkm_wait.
-template <int OFF>
-__device__ __forceinline__ v4s ds_tr16(uint32_t addr) {
-  v4s r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+// 16-byte global load the compiler does not track (no wait is inserted for
+// its result): the caller waits with wait_vmcnt and then claims the value.
+__device__ __forceinline__ v8s load16_async(const void* p) {
+  v8s r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p));
   return r;
 }
-template <int N>
-__device__ __forceinline__ void lgkm_wait() {
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+// 4-byte global load the compiler does not track (same contract)
+__device__ __forceinline__ uint32_t load4_async(const void* p) {
+  uint32_t r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p));
+  return r;
 }
-// ties a register to the preceding lgkm_wait, so no use of it moves above
-__device__ __forceinline__ void lgkm_claim(v4s& r) { asm volatile("" : "+v"(r)); }
+// orders every use of r after the preceding (explicit) wait
+__device__ __forceinline__ void claim(v8s& r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void claim(uint32_t& r) { asm volatile("" : "+v"(r)); }
 
-template <int I>
-using IC = std::integral_constant<int, I>;
-// f(IC<I>{}) for I = B .. E-1, unrolled at compile time
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(IC<B>{});
-    static_for<B + 1, E>(f);
-  }
+// max of v over lanes l and l ^ 32 (v_permlane32_swap exchanges the halves)
+__device__ __forceinline__ float swap_halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Workgroup barrier for the LDS hand-off (a compiler memory barrier too).
+// It drains this wave's LDS reads; the DMA waits come before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -144,20 +157,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
+// wait until at most N vector-memory loads of this wave are outstanding
+// (asm, so it stays ordered with the untracked loads and their claims)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt with vmcnt = N, expcnt and lgkmcnt at their maxima
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N));
 }
 
 template <typename T, int D, int FEAT>
-__global__ __launch_bounds__(kNW<D> * 64, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(PrefillArgs a) {
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
   constexpr int NW = kNW<D>;
   constexpr int NST = kNST<D>;
-  constexpr int PD = NST - 1;          // tiles in flight ahead of the computed one
+  constexpr int TB = kTileBytes<D>;
   constexpr int KQ = D / 16;           // QK mfma steps along D
   constexpr int DC = D / 32;           // PV output chunks of 32 head dims
   constexpr int RB = 2 * D;            // bytes per key row
@@ -210,17 +224,33 @@ __global__ __launch_bounds__(kNW<D> * 64, 1) void prefill_kernel(PrefillArgs a) 
   const int lo_row = a.window_left >= 0 ? max(pos - a.window_left, 0) : 0;
   const uint32_t span_row = static_cast<uint32_t>(hi_row - lo_row);
 
+  const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
+  // first key this wave fetches in a tile (clamped to the last key; the
+  // other rows follow it inside the same 16-key group, hence the same block)
+  auto group_key = [&](int tile) { return min(tile * kKT + wave * RW, L - 1); };
+  // Block ids of this wave's key group for tiles t0 + [0, 64): lane t holds
+  // tile t0 + t (clamped to the last tile).  Loaded ahead in one vector load
+  // and read with v_readlane, so the loop issues no scalar loads.
+  auto load_ids = [&](int t0) -> uint32_t {
+    const int tile = min(t0 + lane, t_end - 1);
+    return load4_async(btab + div_magic(group_key(tile), a.bs_magic));
+  };
+  uint32_t ids = load_ids(t_begin);
+
+  // Q fragments (B operand of S^T = K Q^T).  Loaded by asm, like the K/V
+  // DMA: a load the compiler tracks would get a wait at its first use that
+  // also counts the DMAs in flight.  They complete before the prologue's
+  // DMA wait (loads complete in order) and are claimed after it.
   v8s qf[KQ];
   {
-    const uint16_t* qrow = a.q + ((int64_t)(q0 + tok0 + tk) * a.Hq + head) * D + 8 * g2;
+    const int64_t qtok = row_ok ? q0 + tok0 + tk : q0;  // rows past the tile read a valid row
+    const uint16_t* qrow = a.q + (qtok * a.Hq + head) * D + 8 * g2;
 #pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) {
-      v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-      qf[kk] = row_ok ? *reinterpret_cast<const v8s*>(qrow + 16 * kk) : z;
-    }
+    for (int kk = 0; kk < KQ; ++kk) qf[kk] = load16_async(qrow + 16 * kk);
   }
+  wait_vmcnt<KQ>();  // the block ids (issued before Q) landed
+  claim(ids);
 
-  const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
   const uint16_t* kc = a.kc + (int64_t)g * D;
   const uint16_t* vc = a.vc + (int64_t)g * D;
 
@@ -228,28 +258,20 @@ __global__ __launch_bounds__(kNW<D> * 64, 1) void prefill_kernel(PrefillArgs a) 
   //      bytes wave*RW*RB + i*1024 + 16*l of the tile: key row
   //      wave*RW + i*ROWS_PER_I + l/(RB/16), slot l % (RB/16).
   const uint32_t row_bytes = static_cast<uint32_t>(a.Hkv) * D * 2;
-  int dma_row[NI];                // row of the tile this lane fetches, per instruction
+  const uint32_t smem0 = lds_addr(smem);
+  // the piece that belongs at this lane's slot of instruction i's row
+  auto dma_row = [&](int i) { return wave * RW + i * ROWS_PER_I + lane / (RB / 16); };
+  auto dma_kp = [&](int i) { return ((lane % (RB / 16)) ^ swz_k<D>(dma_row(i))) * 16; };
+  auto dma_vp = [&](int i) { return ((lane % (RB / 16)) ^ swz_v<D>(dma_row(i))) * 16; };
   uint32_t dma_k[NI], dma_v[NI];  // byte offset from the wave's first row (all rows present)
-  uint32_t dma_kp[NI], dma_vp[NI];  // byte offset of the piece within its row
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int rr = i * ROWS_PER_I + lane / (RB / 16);
-    const int r = wave * RW + rr;
-    const int slot = lane % (RB / 16);
-    dma_row[i] = r;
-    dma_kp[i] = (slot ^ swz_k<D>(r)) * 16;  // the piece that belongs at this slot
-    dma_vp[i] = (slot ^ swz_v<D>(r)) * 16;
-    dma_k[i] = rr * row_bytes + dma_kp[i];
-    dma_v[i] = rr * row_bytes + dma_vp[i];
+    const uint32_t rr = i * ROWS_PER_I + lane / (RB / 16);
+    dma_k[i] = rr * row_bytes + dma_kp(i);
+    dma_v[i] = rr * row_bytes + dma_vp(i);
   }
-  // first key this wave fetches in a tile (clamped to the last key; the
-  // other rows follow it inside the same 16-key group, hence the same block)
-  auto group_key = [&](int tile) { return min(tile * kKT + wave * RW, L - 1); };
-  // (a scalar load: the entry is wave-uniform and the table is read-only)
-  auto fetch_id = [&](int tile) -> int {
-    const int idx = div_magic(group_key(min(tile, t_end - 1)), a.bs_magic);
-    return *(const __attribute__((address_space(4))) int32_t*)(btab + idx);
-  };
+  // block id of relative tile jt (< 64 past the loaded chunk's start)
+  auto id_of = [&](int jt) { return __builtin_amdgcn_readlane(static_cast<int>(ids), jt & 63); };
   auto issue_tile = [&](int tile, int blk, int stage) {
     const int kbase = tile * kKT;
     const int gk = group_key(tile);
@@ -257,21 +279,21 @@ __global__ __launch_bounds__(kNW<D> * 64, 1) void prefill_kernel(PrefillArgs a) 
     const int64_t slot0 = (int64_t)blk * a.bs + (gk - gq * a.bs);  // cache slot of key gk
     const char* kb = reinterpret_cast<const char*>(kc) + slot0 * row_bytes;
     const char* vb = reinterpret_cast<const char*>(vc) + slot0 * row_bytes;
-    char* kst = smem + stage * 2 * kTileBytes<D> + wave * RW * RB;
-    char* vst = kst + kTileBytes<D>;
+    const uint32_t kst = smem0 + stage * 2 * TB + wave * RW * RB;
+    const uint32_t vst = kst + TB;
     if (kbase + wave * RW + RW <= L) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        dma16(kb + dma_k[i], kst + i * 1024);
-        dma16(vb + dma_v[i], vst + i * 1024);
+        dma16(kb, dma_k[i], kst + i * 1024);
+        dma16(vb, dma_v[i], vst + i * 1024);
       }
     } else {
       // rows at or past the end repeat key L - 1
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const uint32_t rr = static_cast<uint32_t>(min(kbase + dma_row[i], L - 1) - gk);
-        dma16(kb + (rr * row_bytes + dma_kp[i]), kst + i * 1024);
-        dma16(vb + (rr * row_bytes + dma_vp[i]), vst + i * 1024);
+        const uint32_t rr = static_cast<uint32_t>(min(kbase + dma_row(i), L - 1) - gk);
+        dma16(kb, rr * row_bytes + dma_kp(i), kst + i * 1024);
+        dma16(vb, rr * row_bytes + dma_vp(i), vst + i * 1024);
       }
     }
   };
@@ -284,177 +306,228 @@ __global__ __launch_bounds__(kNW<D> * 64, 1) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dc][e] = 0.0f;
 
-  // ---- prologue: block ids of the first PD + 1 tiles, then the first PD tiles
-  // (t_begin < t_end whenever the tile has a query row: its own key is visible)
-  int ids[PD + 1];
-#pragma unroll
-  for (int p = 0; p <= PD; ++p) ids[p] = fetch_id(t_begin + p);
-#pragma unroll
-  for (int p = 0; p < PD; ++p)
-    if (t_begin + p < t_end) issue_tile(t_begin + p, ids[p], p);
-  // the first tile (and Q) landed; the other issued tiles may stay in flight
-  static_assert(PD <= 2, "prologue wait assumes at most two tiles in flight");
-  if (PD == 2 && t_begin + 1 < t_end) wait_vmcnt<(PD - 1) * 2 * NI>();
-  else wait_vmcnt<0>();
-  lds_barrier();
-
   // logits z: raw score (no softcap / ALiBi) scaled by cz in the exponent, or
   // the finished log2-unit logit with cz = 1
   const float cz = (SOFTCAP || ALIBI) ? 1.0f : a.scale_log2;
-  // K operand rows r32 and 32 + r32 share the swizzle (they differ by 32)
-  const int krow_sw = swz_k<D>(r32);
+  // does any row of this wave see a key of the tile starting at kbase?
+  auto tile_active = [&](int kbase) {
+    bool act = w_rows;
+    if (a.causal) act = act && kbase <= w_pmax;
+    if (a.window_left >= 0) act = act && kbase + kKT - 1 >= w_pmin - a.window_left;
+    return act;
+  };
 
-  int stage = 0;
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    const bool more = tile + PD < t_end;
-    if (more) {
-      const int next_id = fetch_id(tile + PD + 1);
-      issue_tile(tile + PD, ids[PD], (stage + PD) % NST);
+  // ---- K operand of S^T = K Q^T: rows h2*32 + r32 of the tile, 16-byte piece
+  //      2*kk + g2 (swizzled); rows r32 and 32 + r32 share the swizzle
+  uint32_t k_lane[KQ];
 #pragma unroll
-      for (int p = 0; p < PD - 1; ++p) ids[p + 1] = ids[p + 2];
-      ids[PD] = next_id;
-    }
+  for (int kk = 0; kk < KQ; ++kk)
+    k_lane[kk] = r32 * RB + 16 * ((2 * kk + g2) ^ swz_k<D>(r32));
 
-    const int kbase = tile * kKT;
-    bool active = w_rows;
-    if (a.causal) active = active && kbase <= w_pmax;
-    if (a.window_left >= 0) active = active && kbase + kKT - 1 >= w_pmin - a.window_left;
+  // ---- V operand of O^T += V^T P^T: step s holds V[16s + 4*g2 + [0,4)][d] and
+  //      V[16s + 8 + 4*g2 + [0,4)][d] for d = dc*32 + r32, two transpose reads.
+  //      Lane j of each 16-lane group points at row k0 + j/4, head dims
+  //      c0 + 4*(j%4) with c0 = dc*32 + 16*((lane >> 4) & 1).  With the
+  //      swizzle, the 16-byte piece of head dim d = dc*32 + vd in row r is
+  //      4*(dc ^ x) + vd/8 with x = swz_v(r)/4 < 4, i.e. lane address m = dc & 3
+  //      plus the immediate 64*(dc & ~3).
+  constexpr int NM = DC < 4 ? DC : 4;
+  uint32_t v_lane[NM];
+  {
+    const int vr = 4 * g2 + ((lane & 15) >> 2);              // row within a 16-key step
+    const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // head dim within a chunk
+    const int x = swz_v<D>(vr) >> 2;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) v_lane[m] = vr * RB + 64 * (m ^ x) + 16 * (vd >> 3) + 2 * (vd & 7);
+  }
 
-    if (active) {
-      const uint16_t* ks = reinterpret_cast<const uint16_t*>(smem + stage * 2 * kTileBytes<D>);
-      const uint16_t* vs = ks + kTileBytes<D> / 2;
-
-      // ---- S^T = K Q^T for keys kbase + [0, 32) and [32, 64)
-      v16f sacc[2];
+  // ---- softmax of one tile's scores (lane holds keys
+  //      kbase + 32*h2 + 8*(e/4) + 4*g2 + e%4 of its row): logits, masks on
+  //      tiles that cut a row's visible range, lazy rescale, probabilities
+  //      packed as the B operand of the PV product
+  auto softmax = [&](v16f* sacc, int kbase, v8s* pb) {
+    const bool need_mask = kbase + kKT > L || (a.causal && kbase + kKT - 1 > w_pmin) ||
+                           (a.window_left >= 0 && kbase < w_pmax - a.window_left);
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
-        const uint16_t* krow = ks + (h2 * 32 + r32) * D;
-#pragma unroll
-        for (int kk = 0; kk < KQ; ++kk)
-          sacc[h2] = T::mfma32x32x16(
-              *reinterpret_cast<const v8s*>(krow + (((2 * kk + g2) ^ krow_sw) << 3)), qf[kk],
-              sacc[h2]);
+      for (int e = 0; e < 16; ++e) {
+        float z = sacc[h2][e];
+        const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if constexpr (SOFTCAP) z = a.cap_log2 * tanh_f32(z * a.scale_over_cap);
+        else if constexpr (ALIBI) z = z * a.scale_log2;
+        if constexpr (ALIBI) z -= slope_log2 * static_cast<float>(abs(pos - key));
+        sacc[h2][e] = z;
       }
-
-      // ---- logits; lane holds keys kbase + 32*h2 + 8*(e/4) + 4*g2 + e%4 of its row
-      const bool need_mask = kbase + kKT > L || (a.causal && kbase + kKT - 1 > w_pmin) ||
-                             (a.window_left >= 0 && kbase < w_pmax - a.window_left);
+    if (need_mask) {
+      // visible iff 0 <= key - lo_row <= span_row (unsigned compare)
+      const int base = kbase + 4 * g2 - lo_row;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float z = sacc[h2][e];
-          const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-          if constexpr (SOFTCAP) z = a.cap_log2 * tanh_f32(z * a.scale_over_cap);
-          else if constexpr (ALIBI) z = z * a.scale_log2;
-          if constexpr (ALIBI) z -= slope_log2 * static_cast<float>(abs(pos - key));
-          sacc[h2][e] = z;
+          const uint32_t rel = static_cast<uint32_t>(base + 32 * h2 + 8 * (e >> 2) + (e & 3));
+          sacc[h2][e] = rel <= span_row ? sacc[h2][e] : kNegInf;
         }
-      if (need_mask) {
-        // visible iff 0 <= key - lo_row <= span_row (unsigned compare)
-        const int base = kbase + 4 * g2 - lo_row;
+    }
+    // row max: a max3 tree over the lane's 32 scores, then the other half of
+    // the row (lane ^ 32) through a lane swap
+    float m1[11];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+    for (int i = 0; i < 10; ++i) {
+      const int e = 3 * i;
+      m1[i] = fmaxf(fmaxf(sacc[e >> 4][e & 15], sacc[(e + 1) >> 4][(e + 1) & 15]),
+                    sacc[(e + 2) >> 4][(e + 2) & 15]);
+    }
+    m1[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
+    const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+    const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
+    const float m2d = fmaxf(m1[9], m1[10]);
+    float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
+    mx = fmaxf(mx, swap_halves_max(mx));
+    const float m_tile = mx * cz;
+
+    // lazy rescale: move the reference only when the max grew a lot; rows
+    // that do not grow keep alpha = 1
+    const bool grow = m_tile > m_run + kTau;
+    if (wave_any(grow)) {
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
+      l_run *= alpha;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t rel = static_cast<uint32_t>(base + 32 * h2 + 8 * (e >> 2) + (e & 3));
-            sacc[h2][e] = rel <= span_row ? sacc[h2][e] : kNegInf;
-          }
+      for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == kNegInf ? 0.0f : -m_run;
+
+    float ps[4];  // sums of the rounded probabilities the PV product uses
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], cz, neg_m));
+      u32x4 w = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
+                 T::pack2(pv[6], pv[7])};
+      ps[s] = T::sum2(w[3], T::sum2(w[2], T::sum2(w[1], T::sum2(w[0], 0.0f))));
+      pb[s] = __builtin_bit_cast(v8s, w);
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // MFMA block: PV of the previous tile (if HAS_PV), then S^T of this tile
+  // (if HAS_QK); vst / kst are LDS byte addresses of the V and K tiles
+  auto mfma_block = [&](auto has_pv, auto has_qk, uint32_t vst, uint32_t kst, const v8s* pb,
+                        v16f* sacc) {
+    constexpr bool HPV = decltype(has_pv)::value;
+    constexpr bool HQK = decltype(has_qk)::value;
+    // each section is a scheduling region of its own (the read/MFMA
+    // interleave below is pinned per region)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (HPV) {
+      const char* vs = smem + (vst - smem0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const char* p = vs + v_lane[dc & 3] + 16 * s * RB + 64 * (dc & ~3);
+          const v4s lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(p));
+          const v4s hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(p + 8 * RB));
+          const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dc] = T::mfma32x32x16(av, pb[s], oacc[dc]);
+        }
+      // schedule: 8 reads ahead, then one MFMA per two reads
+      constexpr int NR = 8 * DC, LEAD = 8, MID = (NR - LEAD) / 2;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < MID; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
-      float mx = kNegInf;
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DC - MID, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (HQK) {
+      const char* ks = smem + (kst - smem0);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_tile = mx * cz;
-
-      // ---- lazy rescale: move the reference only when the max grew a lot;
-      //      rows that do not grow keep alpha = 1
-      const bool grow = m_tile > m_run + kTau;
-      if (wave_any(grow)) {
-        const float m_new = grow ? m_tile : m_run;
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
-        l_run *= alpha;
+        for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
+      // (reads written out first: the pinned interleave below then applies)
+      v8s kf[2 * KQ];
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
-        m_run = m_new;
+      for (int kk = 0; kk < KQ; ++kk)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          kf[2 * kk + h2] = *reinterpret_cast<const v8s*>(ks + k_lane[kk] + h2 * 32 * RB);
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) sacc[h2] = T::mfma32x32x16(kf[2 * kk + h2], qf[kk], sacc[h2]);
+      // schedule: 6 reads ahead, then one MFMA per read
+      constexpr int NR = 2 * KQ, LEAD = 6;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < NR - LEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
-      const float neg_m = m_run == kNegInf ? 0.0f : -m_run;
-
-      float psum = 0.0f;  // sum of the rounded probabilities the PV product uses
-      v8s pb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], cz, neg_m));
-        u32x4 w = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
-                   T::pack2(pv[6], pv[7])};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) psum = T::sum2(w[e], psum);
-        pb[s] = __builtin_bit_cast(v8s, w);
-      }
-      l_run += psum;
-
-      // ---- O^T += V^T P^T; the A operand of step s holds V[16s + 4*g2 + [0,4)][d] and
-      //      V[16s + 8 + 4*g2 + [0,4)][d] for d = dc*32 + r32: two transpose reads.
-      //      Lane j of each 16-lane group points at row k0 + j/4, head dims
-      //      c0 + 4*(j%4) with c0 = dc*32 + 16*((lane >> 4) & 1).  With the
-      //      swizzle, the 16-byte piece of head dim d = dc*32 + vd in row r is
-      //      4*(dc ^ x) + vd/8 with x = swz_v(r)/4 < 4, i.e. lane address m = dc & 3
-      //      plus the immediate 64*(dc & ~3).
-      {
-        const int vr = 4 * g2 + ((lane & 15) >> 2);              // row within a 16-key step
-        const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // head dim within a chunk
-        const uint32_t vbase = lds_addr(vs) + vr * RB + 16 * (vd >> 3) + 2 * (vd & 7);
-        const int x = swz_v<D>(vr) >> 2;
-        constexpr int NM = DC < 4 ? DC : 4;
-        uint32_t va[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) va[m] = vbase + 64 * (m ^ x);
-        v4s buf[2][2 * DC];
-        // the 2 * DC reads of step S into b
-        auto issue = [&](auto s_c, v4s* bb) {
-          constexpr int S = decltype(s_c)::value;
-          static_for<0, DC>([&](auto dc_c) {
-            constexpr int dc = decltype(dc_c)::value;
-            constexpr int off = 16 * S * RB + 64 * (dc & ~3);
-            bb[2 * dc] = ds_tr16<off>(va[dc & 3]);
-            bb[2 * dc + 1] = ds_tr16<off + 8 * RB>(va[dc & 3]);
-          });
-        };
-        issue(IC<0>{}, buf[0]);
-        static_for<0, 4>([&](auto s_c) {
-          constexpr int S = decltype(s_c)::value;
-          // reads of step S + 1 go out before step S's products
-          if constexpr (S + 1 < 4) {
-            issue(IC<S + 1>{}, buf[(S + 1) & 1]);
-            lgkm_wait<(2 * DC < 15 ? 2 * DC : 15)>();  // (15: the field maximum)
-          } else {
-            lgkm_wait<0>();
-          }
-#pragma unroll
-          for (int dc = 0; dc < DC; ++dc) {
-            v4s& lo = buf[S & 1][2 * dc];
-            v4s& hi = buf[S & 1][2 * dc + 1];
-            lgkm_claim(lo);
-            lgkm_claim(hi);
-            const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[dc] = T::mfma32x32x16(av, pb[S], oacc[dc]);
-          }
-        });
-      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LEAD, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    // the next tile landed (later ones may stay in flight); all waves are
-    // done reading the stage the next DMA reuses
-    if (more) wait_vmcnt<(PD - 1) * 2 * NI>();
+  // ---- prologue: the first NST - 1 tiles
+  // (t_begin < t_end whenever the tile has a query row: its own key is visible)
+  const int n = t_end - t_begin;
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < n) issue_tile(t_begin + p, id_of(p), p);
+  // the first tile (and Q) landed; the other issued tiles may stay in flight
+  static_assert(NST >= 2 && NST <= 4, "waits assume at most two tiles in flight past the next");
+  if (NST >= 4 && n >= 3) wait_vmcnt<4 * NI>();
+  else if (NST >= 3 && n >= 2) wait_vmcnt<2 * NI>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+#pragma unroll
+  for (int kk = 0; kk < KQ; ++kk) {
+    claim(qf[kk]);
+    const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!row_ok) qf[kk] = z;
+  }
+
+  // ---- main loop over key tiles j: tile j + NST - 1 goes into the stage of
+  //      tile j - 1 (all waves passed the barrier after reading it); S^T,
+  //      softmax and PV of tile j; then tile j + 1 must have landed before
+  //      the barrier.
+  int st = 0;  // stage of tile j
+  for (int j = 0; j < n; ++j) {
+    const int tile = t_begin + j;
+    const int kbase = tile * kKT;
+    const int pst = st == 0 ? NST - 1 : st - 1;  // stage of tile j - 1
+    if (j + NST - 1 < n) {
+      const int jt = j + NST - 1;
+      if ((jt & 63) == 0) {  // next chunk of block ids (every 64 tiles)
+        ids = load_ids(t_begin + jt);
+        wait_vmcnt<0>();
+        claim(ids);
+      }
+      issue_tile(tile + NST - 1, id_of(jt), pst);
+    }
+    const bool act = tile_active(kbase);
+    const uint32_t kst = smem0 + st * 2 * TB;
+    v16f sacc[2];
+    v8s pb[4];
+    if (act) mfma_block(std::false_type{}, std::true_type{}, 0u, kst, pb, sacc);
+    if (act) softmax(sacc, kbase, pb);
+    if (act) mfma_block(std::true_type{}, std::false_type{}, kst + TB, 0u, pb, sacc);
+    // tile j + 1 landed (the tiles issued after it may stay in flight)
+    const int ahead = min(j + NST - 1, n - 1) - (j + 1);
+    if (NST >= 4 && ahead >= 2) wait_vmcnt<4 * NI>();
+    else if (NST >= 3 && ahead == 1) wait_vmcnt<2 * NI>();
     else wait_vmcnt<0>();
     lds_barrier();
-    stage = stage + 1 == NST ? 0 : stage + 1;
+    st = st + 1 == NST ? 0 : st + 1;
   }
 
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
