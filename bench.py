@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 METRIC = "decode KV-read GB/s + prefill attn TFLOP/s, bf16 paged KV, 1×MI355X"
+WARM_SECONDS = 0.3  # untimed warm-up after --warmup steps, before each timed region
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
@@ -150,7 +151,7 @@ def run_decode(args, pa, runner, w):
 
     for i in range(args.warmup):
         step(i, False)
-    torch.cuda.synchronize()
+    spin_up(lambda: step(0, False))
     # whole-step wall time without the per-kernel events
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -167,6 +168,17 @@ def run_decode(args, pa, runner, w):
                 tokens=int(s.numel()))
 
 
+def spin_up(fn, seconds: float = WARM_SECONDS):
+    """More untimed warm-up: repeat fn until `seconds` of GPU work have run,
+    so the timed region sees steady-state clocks."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def run_prefill(args, pa, runner):
     w = W.prefill_batch()
     call = w.steps[0].calls[0]
@@ -177,7 +189,8 @@ def run_prefill(args, pa, runner):
     for _ in range(args.warmup):
         pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
         cache.run(cb)
-    torch.cuda.synchronize()
+    spin_up(lambda: (pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s),
+                     cache.run(cb)))
     for _ in range(args.steps):
         with rac_t:
             pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)

@@ -111,12 +111,17 @@ __device__ __forceinline__ int swz_v(int r) {
 // for every LDS DMA in flight before each later LDS read, since it cannot
 // tell the stages apart, which would empty the ring.  The DMA waits are
 // placed by hand instead (wait_vmcnt before the hand-off barrier).  M0,
-// which holds the LDS base, is restored afterwards.
+// which holds the LDS base, is restored afterwards.  The s_nop covers the
+// GFX9 hazards of an LDS DMA that reads M0 right after an SALU write of M0
+// (one wait state) and of a vector-memory instruction that reads an SGPR a
+// VALU instruction wrote (five); without the first, the DMA can take the
+// previous M0 as its LDS base.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
   uint32_t save;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save)
