@@ -100,6 +100,9 @@ int reshape_and_cache(const void* key, const void* value,
  *                   after the softcap.
  *   Query head h reads KV head h / (num_heads / num_kv_heads).
  *   A query that sees no key gets out = 0 and lse = -inf.
+ *   PA_ERR_UNSUPPORTED also for num_seqs > 65535, more than 128 query heads
+ *   per KV head, max_seqlen_k >= 2^24 or num_kv_heads * max_seqlen_q >=
+ *   2^31 (grid limits).
  */
 int paged_attn_prefill(void* out, float* lse, const void* q,
                        const void* key_cache, const void* value_cache,

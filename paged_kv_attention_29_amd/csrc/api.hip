@@ -137,6 +137,10 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 128 query heads per KV head", fn);
   if (max_seqlen_k >= (1 << 24))
     return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
+  if (num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 sequences in one call", fn);
+  if ((int64_t)num_kv_heads * max_seqlen_q > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads * max_seqlen_q must be below 2^31", fn);
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
   pa::AttnParams p{};
   p.out = out;

@@ -62,7 +62,7 @@ struct PrefillArgs {
   const int32_t* block_table;
   int64_t bt_stride;
   int64_t total_q;
-  int B, Hq, Hkv, G, bs, tok_per_tile;
+  int B, Hq, Hkv, G, bs, tok_per_tile, n_qtiles;
   uint32_t bs_magic;
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap
@@ -192,9 +192,16 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   const int r32 = lane & 31;
   const int g2 = lane >> 5;
 
-  const int g = blockIdx.x;
+  // Grid (Hkv * query tiles, sequences), x = tile' * Hkv + g.  Workgroups are
+  // dispatched to the 8 XCDs round-robin in linear order, so with 8 KV heads
+  // XCD g runs every workgroup of head g.  The sequence is the outer index,
+  // so an XCD works through one sequence's query tiles together and the
+  // sequence's K/V for that head (512 B per key at D = 128) stays in the
+  // XCD's L2 while they run.  Inside a sequence the long (late) tiles go
+  // first (tile' counts down from the last tile).
+  const int g = blockIdx.x % a.Hkv;
+  const int qt = a.n_qtiles - 1 - static_cast<int>(blockIdx.x / a.Hkv);
   const int b = blockIdx.y;
-  const int qt = gridDim.z - 1 - blockIdx.z;  // long (late) tiles first
   const int q0 = a.cu_q[b];
   const int nq = a.cu_q[b + 1] - q0;
   const int tok0 = qt * a.tok_per_tile;
@@ -565,9 +572,10 @@ int launch_p(const PrefillArgs& args, int max_seqlen_q, hipStream_t stream) {
   }
   PrefillArgs a = args;
   a.tok_per_tile = kRows<D> / a.G;
-  const int ntiles = (max_seqlen_q + a.tok_per_tile - 1) / a.tok_per_tile;
-  if (ntiles == 0) return 0;
-  const dim3 grid(a.Hkv, a.B, ntiles);
+  a.n_qtiles = (max_seqlen_q + a.tok_per_tile - 1) / a.tok_per_tile;
+  if (a.n_qtiles == 0) return 0;
+  // (the API bounds Hkv * max_seqlen_q below 2^31 and B by 65535)
+  const dim3 grid(static_cast<unsigned>(a.Hkv * a.n_qtiles), a.B, 1);
   hipLaunchKernelGGL((prefill_kernel<T, D, FEAT>), grid, dim3(kNW<D> * 64),
                      prefill_lds_bytes<D>(), stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;

@@ -70,6 +70,7 @@ def test_decode_validation(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(bs=8), -1), (dict(hq=5, hkv=2), -1), (dict(d=32), -2), (dict(out=None), -1),
     (dict(cu=None), -1), (dict(total_q=-1), -1), (dict(dtype=2), -2),
+    (dict(num_seqs=70000), -2), (dict(hq=512, hkv=256, mq=8388609), -2),
 ])
 def test_prefill_validation(lib, kw, code):
     assert _prefill(lib, **kw) == code
