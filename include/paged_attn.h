@@ -120,7 +120,8 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
  * optionally split along the keys [Aphrodite flash_attn.py,
  * FlashAttentionImpl.forward, the flash_attn_with_kvcache decode call;
  * vLLM flash_attn.py (e2f56c3), FlashAttentionMetadataBuilder, num_splits
- * and its [num_splits, num_heads, num_tokens, head_size] intermediates].
+ * and its [num_splits, num_heads, num_tokens, head_size] intermediates;
+ * vLLM flashinfer.py, FlashInferMetadataBuilder, fixed_split_size].
  *
  *   q               [num_seqs, num_heads, head_size] (dtype); the query of
  *                   sequence b sits at position seq_lens[b] - 1.
@@ -130,12 +131,17 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
  *   num_splits  > 1 writes only part_out fp32 [num_splits, num_seqs,
  *                   num_heads, head_size] and part_lse fp32 [num_splits,
  *                   num_heads, num_seqs]; out and lse are not touched (may be
- *                   NULL).  Split p of sequence b covers keys
- *                   [p*c, min((p+1)*c, L)) with c = block_size *
- *                   ceil(ceil(L / num_splits) / block_size); an empty split
- *                   writes part_out = 0, part_lse = -inf.  Combine with
+ *                   NULL).  Every sequence is cut into the same fixed,
+ *                   block-aligned chunks sized from the batch bound:
+ *                   c = block_size * ceil(ceil(max_seq_len / num_splits) /
+ *                   block_size); split p of sequence b covers keys
+ *                   [p*c, min((p+1)*c, L)), and the last split also takes
+ *                   any keys past num_splits*c (so a loose max_seq_len
+ *                   still covers the sequence).  An empty split writes
+ *                   part_out = 0, part_lse = -inf.  Combine with
  *                   merge_attn_states(out, lse, part_out, part_lse,
  *                   num_splits, num_seqs, num_heads, head_size, PA_F32, ...).
+ *   max_seq_len     host upper bound of seq_lens (sizes the splits).
  *   window_left, softcap, alibi_slopes as for prefill.  num_splits <= 256.
  *   num_heads / num_kv_heads must be at most 16.
  */

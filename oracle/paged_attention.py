@@ -173,34 +173,47 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                   alibi_slopes=alibi_slopes, key_ranges=key_ranges)
 
 
-def split_bounds(seq_len: int, num_splits: int, block_size: int):
+def split_bounds(seq_len: int, num_splits: int, block_size: int,
+                 max_seq_len: Optional[int] = None):
     """Key partition of one sequence for split-KV decode.
 
     The pages give the partial-result buffers and their shape
     [num_splits, num_heads, num_tokens, head_size] but not the boundaries
     [vLLM flash_attn.py (e2f56c3), FlashAttentionMetadataBuilder, the
-    max_num_splits note].  Reading used here: equal block-aligned chunks,
-    chunk = block_size * ceil(ceil(L / S) / block_size); split p covers
-    [p * chunk, min((p + 1) * chunk, L)), possibly empty.
+    max_num_splits note], and another backend sizes its KV splits by a
+    fixed number of keys [vLLM flashinfer.py, FlashInferMetadataBuilder,
+    decode_fixed_split_size / fixed_split_size].  Reading used here: every
+    sequence of a batch is cut into the same fixed-size, block-aligned
+    chunks sized from the batch bound max_seq_len,
+        chunk = block_size * ceil(ceil(max_seq_len / S) / block_size),
+    split p covers [p * chunk, min((p + 1) * chunk, L)) (possibly empty),
+    and the last split also takes any keys past S * chunk (a loose bound
+    still covers the sequence).  With max_seq_len = L this is the even
+    division of one sequence.
     """
-    per = -(-seq_len // num_splits)
+    if max_seq_len is None:
+        max_seq_len = seq_len
+    per = -(-max_seq_len // num_splits)
     chunk = block_size * (-(-per // block_size))
     out = []
     for p in range(num_splits):
         lo = min(p * chunk, seq_len)
-        hi = min((p + 1) * chunk, seq_len)
+        hi = seq_len if p == num_splits - 1 else min((p + 1) * chunk, seq_len)
         out.append((lo, hi))
     return out
 
 
 def decode_splits(q, key_cache, value_cache, seq_lens, block_table, scale,
                   num_splits: int, window_left: int = -1, softcap: float = 0.0,
-                  alibi_slopes=None):
+                  alibi_slopes=None, max_seq_len: Optional[int] = None):
     """Partial decode results for each split: parts_out
     [S, num_seqs, num_heads, head_size] and parts_lse [S, num_heads, num_seqs]
-    (float64).  An empty split yields out = 0 and lse = -inf."""
+    (float64).  An empty split yields out = 0 and lse = -inf.  The splits
+    are sized from max_seq_len (default: the longest sequence)."""
     block_size = key_cache.shape[1]
-    bounds = [split_bounds(int(L), num_splits, block_size) for L in seq_lens]
+    if max_seq_len is None:
+        max_seq_len = max(int(L) for L in seq_lens)
+    bounds = [split_bounds(int(L), num_splits, block_size, max_seq_len) for L in seq_lens]
     outs, lses = [], []
     for p in range(num_splits):
         o, l = decode(q, key_cache, value_cache, seq_lens, block_table, scale,

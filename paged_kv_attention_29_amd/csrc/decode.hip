@@ -4,7 +4,10 @@
 // flash_attn.py (e2f56c3), FlashAttentionMetadataBuilder num_splits and its
 // intermediate buffers).
 //
-// Work item = (kv head g, sequence b, split).  The G = Hq / Hkv query heads
+// Work item = (kv head g, sequence b, split).  Splits are fixed chunks of
+// keys sized from the batch bound max_seq_len (vLLM flashinfer.py,
+// FlashInferMetadataBuilder, fixed_split_size), so every non-empty work
+// item of a batch is about the same size.  The G = Hq / Hkv query heads
 // sharing KV head g are the 16 columns of one MFMA tile (padded with zero
 // queries), so each K/V byte is read from HBM once for all G heads.  Keys
 // are processed in tiles of 16 (one MFMA M-tile); block_size is a multiple
@@ -41,6 +44,7 @@ struct DecodeArgs {
   const int32_t* block_table;
   int64_t bt_stride;
   int B, Hq, Hkv, G, bs, S;
+  int chunk;            // keys per split (block-aligned, from the batch bound)
   uint32_t bs_magic;    // ceil(2^32 / bs)
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap
@@ -95,10 +99,10 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
 
   const int L = a.seq_lens[b];
   const int pos = L - 1;
-  const int per = (L + a.S - 1) / a.S;
-  const int chunk = ((per + a.bs - 1) / a.bs) * a.bs;
-  const int lo = min(split * chunk, L);
-  const int hi = min(lo + chunk, L);
+  // split p covers keys [p * chunk, (p + 1) * chunk) of the sequence; the
+  // last split also takes any keys past S * chunk
+  const int lo = static_cast<int>(min((int64_t)split * a.chunk, (int64_t)L));
+  const int hi = split == a.S - 1 ? L : min(lo + a.chunk, L);
   const int lo_vis = a.window_left >= 0 ? max(lo, pos - a.window_left) : lo;
   const int s_begin = lo_vis / KPS;
   const int s_end = (hi + KPS - 1) / KPS;
@@ -368,6 +372,11 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.G = p.num_heads / p.num_kv_heads;
   a.bs = p.block_size;
   a.S = p.num_splits;
+  {
+    // fixed, block-aligned chunks sized from the batch bound max_seq_len
+    const int64_t per = ((int64_t)p.max_seqlen_k + p.num_splits - 1) / p.num_splits;
+    a.chunk = static_cast<int>((per + p.block_size - 1) / p.block_size * p.block_size);
+  }
   a.bs_magic = static_cast<uint32_t>(((1ULL << 32) + p.block_size - 1) / p.block_size);
   const bool softcap = p.softcap > 0.f;
   a.scale_log2 = p.scale * kLog2e;

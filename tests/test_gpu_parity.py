@@ -222,6 +222,36 @@ def test_decode_edges(pa, runner, case):
     assert_lse_close(cb.lse, ref[1], name)
 
 
+@pytest.mark.parametrize("mx", [4096, 1000])
+def test_decode_split_bound(pa, runner, mx):
+    """Splits are sized from the max_seq_len argument: a loose bound leaves
+    empty splits, an under-bound makes the last split take the rest."""
+    _announce(f"decode split bound max_seq_len={mx}")
+    S = 4
+    w = W.custom(f"bound{mx}", 21, [699, 44, 15, 1299], [1, 1, 1, 1], 8, 2, 128, 16,
+                 torch.bfloat16, "decode", num_splits=S)
+    cache = runner.PagedCache(w)
+    cache.fill_context()
+    k, v, s = cache.step_inputs(w.steps[0])
+    pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+    call = w.steps[0].calls[0]
+    cb = cache.call_buffers(call, S)
+    pa.paged_attn_decode(None, cb.q, cache.key_cache, cache.value_cache, cb.seq_lens,
+                         cb.block_table, mx, w.scale, num_splits=S, part_out=cb.part_out,
+                         part_lse=cb.part_lse)
+    pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
+    torch.cuda.synchronize()
+    kc, vc = oracle_cache(w, 0)
+    bt = torch.from_numpy(w.block_table[np.asarray(call.seq_ids)])
+    po, pl = oracle.decode_splits(call.q, kc, vc, call.seq_lens.tolist(), bt, w.scale, S,
+                                  max_seq_len=mx)
+    assert_attn_close(cb.part_out, po, "split parts")
+    assert_lse_close(cb.part_lse, pl, "split lse")
+    ro, rl = oracle.decode(call.q, kc, vc, call.seq_lens.tolist(), bt, w.scale)
+    assert_attn_close(cb.out, ro, "merged")
+    assert_lse_close(cb.lse, rl, "merged lse")
+
+
 PREFILL_EDGES = [
     # name, ctx, q, Hq, Hkv, D, bs, dtype, wl, cap, alibi
     ("ragged_g4", [0, 0, 0, 0, 0], [1, 63, 64, 65, 300], 8, 2, 128, 16, torch.bfloat16, -1, 0.0, False),

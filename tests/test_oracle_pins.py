@@ -328,10 +328,11 @@ def test_decode_equals_last_row_of_prefill():
 # ----------------------------------------------------------------------------
 # a8-a9: split boundaries and merge
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("L,S,bs", [(131072, 32, 16), (1000, 3, 16), (17, 4, 16), (5, 8, 32),
-                                    (4096, 7, 32)])
-def test_split_bounds_partition_block_aligned(L, S, bs):
-    b = oracle.split_bounds(L, S, bs)
+@pytest.mark.parametrize("L,S,bs,mx", [(131072, 32, 16, None), (1000, 3, 16, None),
+                                       (17, 4, 16, None), (5, 8, 32, None), (4096, 7, 32, None),
+                                       (1000, 3, 16, 4096), (700, 8, 16, 4096), (5000, 4, 16, 4096)])
+def test_split_bounds_partition_block_aligned(L, S, bs, mx):
+    b = oracle.split_bounds(L, S, bs, mx)
     assert len(b) == S and b[0][0] == 0 and b[-1][1] == L
     for (lo, hi), (lo2, _) in zip(b, b[1:]):
         assert hi == lo2 and lo <= hi and (lo % bs == 0 or lo == hi == L)
@@ -339,13 +340,26 @@ def test_split_bounds_partition_block_aligned(L, S, bs):
         assert all(hi - lo == 4096 for lo, hi in b)
 
 
-@pytest.mark.parametrize("S", [2, 3, 32])
-def test_split_then_merge_equals_unsplit(S):
+def test_split_bounds_fixed_chunks_from_the_batch_bound():
+    # chunk = 16 * ceil(ceil(4096 / 3) / 16) = 1376 keys: a short sequence sits
+    # in the first split; the others are empty
+    assert oracle.split_bounds(1000, 3, 16, 4096) == [(0, 1000), (1000, 1000), (1000, 1000)]
+    # chunk = 1024; the bound is loose (5000 > 4096): the last split takes the rest
+    assert oracle.split_bounds(5000, 4, 16, 4096) == [(0, 1024), (1024, 2048), (2048, 3072),
+                                                      (3072, 5000)]
+    # every split but the last of a long sequence holds exactly one chunk
+    assert oracle.split_bounds(4000, 8, 32, 4096) == [(512 * p, min(512 * (p + 1), 4000))
+                                                      for p in range(8)]
+
+
+@pytest.mark.parametrize("S,mx", [(2, None), (3, None), (32, None), (4, 640), (3, 100)])
+def test_split_then_merge_equals_unsplit(S, mx):
     lens = [200, 45, 16, 1]
     P = Paged(lens, 2, 16, 16, seed=16)
     q = torch.randn(4, 8, 16)
     slopes = W.alibi_slopes(8)
-    po, pl = oracle.decode_splits(q, P.kc, P.vc, lens, P.table, 0.25, S, 60, 6.0, slopes)
+    po, pl = oracle.decode_splits(q, P.kc, P.vc, lens, P.table, 0.25, S, 60, 6.0, slopes,
+                                  max_seq_len=mx)
     mo, ml = oracle.merge(po, pl)
     o, l = oracle.decode(q, P.kc, P.vc, lens, P.table, 0.25, 60, 6.0, slopes)
     assert torch.allclose(mo, o, atol=1e-12) and torch.allclose(ml, l, atol=1e-12)
