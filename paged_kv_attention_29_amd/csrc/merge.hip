@@ -66,10 +66,29 @@ __global__ __launch_bounds__(256) void merge_kernel(void* __restrict__ out,
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
   float wsum = 0.0f;
   const int64_t part_stride = T * H * D;
-  for (int p = 0; p < S; ++p) {
+  // parts in batches of 8: the loads of a batch are independent and go out
+  // together (one memory latency per batch, not per part)
+  int p = 0;
+  for (; p + 8 <= S; p += 8) {
+    float w[8], x[8][EPL];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w[j] = fast_exp2((parts_lse[(p + j) * lse_stride + lse_off] - m) * kLog2e);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[j][e] = Elem<PT>::ld(parts, (p + j) * part_stride + row + e);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      wsum += w[j];
+      // an empty part (w = 0) may hold anything, finite or not
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += w[j] != 0.0f ? w[j] * x[j][e] : 0.0f;
+    }
+  }
+  for (; p < S; ++p) {
     const float w = fast_exp2((parts_lse[p * lse_stride + lse_off] - m) * kLog2e);
     wsum += w;
-    if (w == 0.0f) continue;  // an empty part may hold anything finite or not
+    if (w == 0.0f) continue;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] += w * Elem<PT>::ld(parts, p * part_stride + row + e);
   }
