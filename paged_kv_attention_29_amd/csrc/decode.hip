@@ -56,35 +56,40 @@ struct DecodeArgs {
 enum { kSoftcap = 1, kAlibi = 2 };
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// Keys per iteration: NT MFMA row tiles of 16 (two for D <= 128, so a wave
-// keeps 16 KB of K/V in flight while it computes the previous 32 keys).
-template <int D>
-constexpr int kNT = D <= 128 ? 2 : 1;
+// A work item covers HPW adjacent KV heads (2 when the head counts allow it
+// and D <= 128): each key row of the item is then 2 * 256 contiguous bytes,
+// which the memory system streams faster than 256-byte rows 2 KB apart.
+// Their query heads are the first G * HPW columns of the MFMA tile.
+// Keys per iteration: NT MFMA row tiles of 16, so that a wave keeps 16 KB of
+// K/V in flight while it computes the previous step (one tile for two heads
+// or D = 256).
+template <int D, int HPW>
+constexpr int kNT = (D <= 128 && HPW == 1) ? 2 : 1;
 
 // LDS: per-wave V slabs of 16 * NT rows (pitch D + 16 elements: the 32-byte
 // pad spreads the 16 rows a transpose read touches over all banks), reused
 // after the key loop for the cross-wave combine: [wave][head j < G][m, l, O].
-template <int D>
-constexpr int kVPitch = D + 16;
-template <int D>
+template <int D, int HPW>
+constexpr int kVPitch = HPW * D + 16;
+template <int D, int HPW>
 constexpr size_t decode_lds_bytes(int G) {
-  const size_t v = (size_t)kWaves * 16 * kNT<D> * kVPitch<D> * 2;
-  const size_t c = (size_t)kWaves * G * (D + 2) * 4;
+  const size_t v = (size_t)kWaves * 16 * kNT<D, HPW> * kVPitch<D, HPW> * 2;
+  const size_t c = (size_t)kWaves * G * HPW * (D + 2) * 4;
   return v > c ? v : c;
 }
 
 template <int D>
 constexpr int kMinBlocks = D <= 128 ? 2 : 1;
 
-template <typename T, int D, int FEAT>
+template <typename T, int D, int FEAT, int HPW>
 __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(DecodeArgs a) {
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
   constexpr int KK = D / 32;   // QK mfma steps along D
   constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
-  constexpr int NT = kNT<D>;
+  constexpr int NT = kNT<D, HPW>;
   constexpr int KPS = 16 * NT; // keys per step
-  constexpr int P = kVPitch<D>;
+  constexpr int P = kVPitch<D, HPW>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -92,8 +97,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int r16 = lane & 15;   // key row of the K piece / head column of the tile
   const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
 
-  const int g = blockIdx.x % a.Hkv;
-  const int rest = blockIdx.x / a.Hkv;
+  const int g0 = (blockIdx.x % (a.Hkv / HPW)) * HPW;  // first KV head of the item
+  const int rest = blockIdx.x / (a.Hkv / HPW);
   const int b = rest % a.B;
   const int split = rest / a.B;
 
@@ -107,30 +112,36 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int s_begin = lo_vis / KPS;
   const int s_end = (hi + KPS - 1) / KPS;
 
-  const int head = g * a.G + r16;  // query head of this lane's column
-  const bool col_ok = r16 < a.G;
+  const int GC = a.G * HPW;          // used columns
+  const int head = g0 * a.G + r16;  // query head of this lane's column
+  const bool col_ok = r16 < GC;
+  const int hsel = r16 / a.G;       // which of the item's KV heads the column reads
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = col_ok ? a.alibi[head] * kLog2e : 0.0f;
 
-  // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8
-  v8s qf[KK];
+  // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8; with
+  // two KV heads, operand h is zero outside head h's columns, so the two
+  // products accumulate into one S^T tile
+  v8s qf[HPW][KK];
   {
     const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + head) * D + c4 * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-      qf[kk] = col_ok ? *reinterpret_cast<const v8s*>(qrow + kk * 32) : z;
+      const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+      const v8s qv = col_ok ? *reinterpret_cast<const v8s*>(qrow + kk * 32) : z;
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) qf[h][kk] = hsel == h ? qv : z;
     }
   }
 
   const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive slots
-  const uint16_t* kcg = a.kc + (int64_t)g * D + c4 * 8;
-  const uint16_t* vcg = a.vc + (int64_t)g * D + c4 * 8;
+  const uint16_t* kcg = a.kc + (int64_t)g0 * D + c4 * 8;
+  const uint16_t* vcg = a.vc + (int64_t)g0 * D + c4 * 8;
 
   struct Frag {
-    v8s k[NT][KK];
-    v8s v[NT][KK];
+    v8s k[HPW][NT][KK];
+    v8s v[HPW][NT][KK];
   };
   // Block ids of a step's tiles.  Loads are branch-free (so the compiler can
   // count outstanding loads exactly): a tile starting at or past hi is
@@ -153,10 +164,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
       const uint16_t* kp = kcg + slot * row_stride;
       const uint16_t* vp = vcg + slot * row_stride;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        f.k[nt][kk] = *reinterpret_cast<const v8s*>(kp + kk * 32);
-        f.v[nt][kk] = *reinterpret_cast<const v8s*>(vp + kk * 32);
-      }
+      for (int h = 0; h < HPW; ++h)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          f.k[h][nt][kk] = *reinterpret_cast<const v8s*>(kp + h * D + kk * 32);
+          f.v[h][nt][kk] = *reinterpret_cast<const v8s*>(vp + h * D + kk * 32);
+        }
     }
   };
 
@@ -177,7 +190,9 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
       // ---- scores S^T[key j0 + 4*c4 + e][head r16], in log2 units
       v4f sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc = T::mfma16x16x32(f.k[nt][kk], qf[kk], sc);
+      for (int h = 0; h < HPW; ++h)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sc = T::mfma16x16x32(f.k[h][nt][kk], qf[h][kk], sc);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = j0 + 4 * c4 + e;
@@ -224,10 +239,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
       const bool row_ok = key >= lo_vis && key < hi;
       uint16_t* dst = vs + (16 * nt + r16) * P + c4 * 8;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-        *reinterpret_cast<v8s*>(dst + kk * 32) = row_ok ? f.v[nt][kk] : z;
-      }
+      for (int h = 0; h < HPW; ++h)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+          *reinterpret_cast<v8s*>(dst + h * D + kk * 32) = row_ok ? f.v[h][nt][kk] : z;
+        }
     }
     wave_lds_sync();
     // ---- O^T[d][head] += V^T[d][key] P^T[key][head]; lane group c4 reads
@@ -247,8 +264,16 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
     } else {
       const u32x2 pq = {pw[0], pw[1]};
       const v4s pb = __builtin_bit_cast(v4s, pq);
+      // with two KV heads, P is split by column: head h's V only meets the
+      // probabilities of head h's columns
+      const v4s z = {0, 0, 0, 0};
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) o[dc] = T::mfma16x16x16(lds_read_tr16(vb + dc * 16), pb, o[dc]);
+      for (int h = 0; h < HPW; ++h) {
+        const v4s pbh = (HPW == 1 || hsel == h) ? pb : z;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          o[dc] = T::mfma16x16x16(lds_read_tr16(vb + h * D + dc * 16), pbh, o[dc]);
+      }
     }
     wave_lds_sync();
   };
@@ -282,10 +307,10 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   float l_tot = l_run + shfl_xor(l_run, 16);
   l_tot += shfl_xor(l_tot, 32);
   __syncthreads();  // every wave is done with its V slab
-  float* comb = reinterpret_cast<float*>(smem);  // [wave][G][D + 2]: m, l, O[D]
+  float* comb = reinterpret_cast<float*>(smem);  // [wave][GC][D + 2]: m, l, O[D]
   constexpr int CP = D + 2;
   if (col_ok) {
-    float* row = comb + (wave * a.G + r16) * CP;
+    float* row = comb + (wave * GC + r16) * CP;
     if (c4 == 0) {
       row[0] = m_run;
       row[1] = l_tot;
@@ -297,24 +322,24 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   }
   __syncthreads();
   const bool split_out = a.S > 1;
-  for (int idx = threadIdx.x; idx < a.G * D; idx += kWaves * 64) {
+  for (int idx = threadIdx.x; idx < GC * D; idx += kWaves * 64) {
     const int j = idx / D;
     const int d = idx - j * D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb[(w * a.G + j) * CP]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb[(w * GC + j) * CP]);
     float num = 0.f, den = 0.f;
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float* row = comb + (w * a.G + j) * CP;
+        const float* row = comb + (w * GC + j) * CP;
         const float fw = fast_exp2(row[0] - M);
         den += fw * row[1];
         num += fw * row[2 + d];
       }
     }
     const float val = den > 0.f ? num / den : 0.f;
-    const int h = g * a.G + j;
+    const int h = g0 * a.G + j;
     const float lse = den > 0.f ? (M + __log2f(den)) * kLn2 : kNegInf;
     if (split_out) {
       a.part_out[(((int64_t)split * a.B + b) * a.Hq + h) * D + d] = val;
@@ -326,12 +351,20 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   }
 }
 
+template <typename T, int D, int FEAT, int HPW>
+int launch_h(const DecodeArgs& args, hipStream_t stream) {
+  const int64_t grid = (int64_t)(args.Hkv / HPW) * args.B * args.S;
+  hipLaunchKernelGGL((decode_kernel<T, D, FEAT, HPW>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kWaves * 64), (decode_lds_bytes<D, HPW>(args.G)), stream, args);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 template <typename T, int D, int FEAT>
 int launch_d(const DecodeArgs& args, hipStream_t stream) {
-  const int64_t grid = (int64_t)args.Hkv * args.B * args.S;
-  hipLaunchKernelGGL((decode_kernel<T, D, FEAT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kWaves * 64), decode_lds_bytes<D>(args.G), stream, args);
-  return hipGetLastError() == hipSuccess ? 0 : -3;
+  if constexpr (D <= 128) {
+    if (args.Hkv % 2 == 0 && 2 * args.G <= 16) return launch_h<T, D, FEAT, 2>(args, stream);
+  }
+  return launch_h<T, D, FEAT, 1>(args, stream);
 }
 
 template <typename T, int D>
