@@ -9,7 +9,10 @@ gfx950 assembly of every prefill instantiation:
    (loads complete in issue order: a wait with N no larger than the number
    of untracked loads issued after it covers it);
 2. every LDS DMA follows its M0 write by at least one wait state (the GFX9
-   hazard of an LDS DMA reading M0 right after an SALU write of M0).
+   hazard of an LDS DMA reading M0 right after an SALU write of M0);
+3. no kernel of the library writes through the scalar data cache (scalar
+   stores or atomics, its write-back or discard): stores and atomics
+   (including the decode work counter) are vector-memory instructions.
 
 CPU only: it compiles the kernel source with hipcc (skipped if hipcc is
 missing)."""
@@ -102,3 +105,18 @@ def test_lds_dma_waits_after_m0_write(prefill_asm):
                 assert any(x.startswith("s_nop") for x in between), \
                     f"{name}: LDS DMA issued right after its M0 write"
     assert n_dma > 0
+
+
+@pytest.mark.parametrize("src", ["prefill.hip", "decode.hip", "merge.hip", "reshape_and_cache.hip"])
+def test_no_scalar_cache_writes(src, tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = tmp_path / (src + ".s")
+    subprocess.run([hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang",
+                    "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S",
+                    os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
+    bad = [l.strip() for l in out.read_text().split("\n")
+           if re.match(r"\s*(s_atomic|s_store|s_buffer_store|s_scratch_store|s_dcache_wb|"
+                       r"s_dcache_discard)", l)]
+    assert not bad, f"{src}: {bad[:3]}"
