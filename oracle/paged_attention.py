@@ -128,8 +128,8 @@ def attend(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
     for b in range(len(seq_lens)):
         q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
         n_q, L = q1 - q0, int(seq_lens[b])
-        if n_q == 0:
-            continue
+        if n_q == 0 or L == 0:
+            continue    # no keys: the rows keep out = 0, lse = -inf
         ctx = L - n_q
         q_pos = ctx + torch.arange(n_q, dtype=torch.long)
         vis = _visible(q_pos, L, causal, window_left,

@@ -251,6 +251,22 @@ def test_single_key_returns_that_value():
         assert torch.allclose(l[:, b], sc, atol=1e-14)
 
 
+def test_sequence_without_keys_gives_zero_and_neg_inf():
+    """A decode row of a zero-length sequence sees no key: out 0, lse -inf,
+    and the other rows are those of the batch without it."""
+    P = Paged([0, 1, 21], 2, 8, 16, seed=7)
+    q = torch.randn(3, 4, 8)
+    o, l = oracle.decode(q, P.kc, P.vc, [0, 1, 21], P.table, 0.5)
+    assert torch.equal(o[0], torch.zeros(4, 8, dtype=torch.float64))
+    assert torch.isneginf(l[:, 0]).all()
+    o2, l2 = oracle.decode(q[1:], P.kc, P.vc, [1, 21], P.table[1:], 0.5)
+    assert torch.equal(o[1:], o2) and torch.equal(l[:, 1:], l2)
+    assert torch.equal(o[1], P.V[1][0].double().repeat_interleave(2, dim=0))
+    po, pl = oracle.decode_splits(q, P.kc, P.vc, [0, 1, 21], P.table, 0.5, 3)
+    assert torch.equal(po[:, 0], torch.zeros(3, 4, 8, dtype=torch.float64))
+    assert torch.isneginf(pl[:, :, 0]).all()
+
+
 def test_huge_softcap_equals_no_softcap():
     P = Paged([30, 12], 2, 16, 16, seed=8)
     q = torch.randn(2, 4, 16)
