@@ -97,10 +97,18 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int r16 = lane & 15;   // key row of the K piece / head column of the tile
   const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
 
-  const int g0 = (blockIdx.x % (a.Hkv / HPW)) * HPW;  // first KV head of the item
-  const int rest = blockIdx.x / (a.Hkv / HPW);
-  const int b = rest % a.B;
-  const int split = rest / a.B;
+  // Item order: split-major; within split p the (KV-head group, sequence)
+  // pairs are rotated by p groups.  Workgroup i runs on XCD i % 8 and, within
+  // it, on the shader engines in turn, so without the rotation all splits of
+  // a sequence would land on the same XCDs and engines and long sequences
+  // would load some of them more than others.
+  const int HG = a.Hkv / HPW;
+  const int per_split = HG * a.B;
+  const int split = blockIdx.x / per_split;
+  int j = blockIdx.x - split * per_split - static_cast<int>((int64_t)split * HG % per_split);
+  if (j < 0) j += per_split;
+  const int g0 = (j % HG) * HPW;  // first KV head of the item
+  const int b = j / HG;
 
   const int L = a.seq_lens[b];
   const int pos = L - 1;
@@ -111,6 +119,22 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int lo_vis = a.window_left >= 0 ? max(lo, pos - a.window_left) : lo;
   const int s_begin = lo_vis / KPS;
   const int s_end = (hi + KPS - 1) / KPS;
+  const bool split_out = a.S > 1;
+  if (lo_vis >= hi) {
+    // no visible key: zero output, -inf log-sum-exp
+    for (int idx = threadIdx.x; idx < a.G * HPW * D; idx += kWaves * 64) {
+      const int h = g0 * a.G + idx / D;
+      const int d = idx % D;
+      if (split_out) {
+        a.part_out[(((int64_t)split * a.B + b) * a.Hq + h) * D + d] = 0.f;
+        if (d == 0) a.part_lse[((int64_t)split * a.Hq + h) * a.B + b] = kNegInf;
+      } else {
+        static_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + h) * D + d] = T::from_float(0.f);
+        if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.B + b] = kNegInf;
+      }
+    }
+    return;
+  }
 
   const int GC = a.G * HPW;          // used columns
   const int head = g0 * a.G + r16;  // query head of this lane's column
@@ -321,7 +345,6 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
       for (int e = 0; e < 4; ++e) row[2 + dc * 16 + 4 * c4 + e] = o[dc][e];
   }
   __syncthreads();
-  const bool split_out = a.S > 1;
   for (int idx = threadIdx.x; idx < GC * D; idx += kWaves * 64) {
     const int j = idx / D;
     const int d = idx - j * D;
