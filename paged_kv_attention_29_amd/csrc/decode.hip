@@ -19,10 +19,11 @@
 // K is loaded from HBM straight into the A-operand layout (16-byte pieces of
 // a key row per lane).  V needs its key index inside each lane, so each wave
 // writes its V tile to a private LDS slab row-major and reads it back with
-// the LDS transpose read (one ds_read_b64_tr_b16 per PV MFMA).  The 4 waves of a workgroup take interleaved tiles of the
-// split with their own online-softmax state (fp32, base-2 exponent) and are
-// merged through LDS at the end.  The loads of the next tile are issued
-// before the current tile is computed.
+// the LDS transpose read (one ds_read_b64_tr_b16 per PV MFMA).  The 4 waves
+// of a workgroup take interleaved steps of an item with their own
+// online-softmax state (fp32, base-2 exponent) and are merged through LDS at
+// the item's end.  The loads of a wave's next step are issued before its
+// current step is computed.
 #include "common.h"
 #include "launch.h"
 
@@ -67,122 +68,110 @@ template <int D, int HPW>
 constexpr int kNT = (D <= 128 && HPW == 1) ? 2 : 1;
 
 // LDS: per-wave V slabs of 16 * NT rows (pitch D + 16 elements: the 32-byte
-// pad spreads the 16 rows a transpose read touches over all banks), reused
-// after the key loop for the cross-wave combine: [wave][head j < G][m, l, O].
+// pad spreads the 16 rows a transpose read touches over all banks) and the
+// cross-wave combine area [wave][head j < G * HPW][m, l, pad, pad, O[D]]
+// (fp32).
 template <int D, int HPW>
 constexpr int kVPitch = HPW * D + 16;
 template <int D, int HPW>
+constexpr size_t vslab_bytes() {
+  return (size_t)kWaves * 16 * kNT<D, HPW> * kVPitch<D, HPW> * 2;
+}
+template <int D, int HPW>
+constexpr size_t comb_bytes(int G) {
+  return (size_t)kWaves * G * HPW * (D + 4) * 4;
+}
+// the combine runs after the key loop and reuses the V slabs
+template <int D, int HPW>
 constexpr size_t decode_lds_bytes(int G) {
-  const size_t v = (size_t)kWaves * 16 * kNT<D, HPW> * kVPitch<D, HPW> * 2;
-  const size_t c = (size_t)kWaves * G * HPW * (D + 2) * 4;
-  return v > c ? v : c;
+  return vslab_bytes<D, HPW>() > comb_bytes<D, HPW>(G) ? vslab_bytes<D, HPW>()
+                                                        : comb_bytes<D, HPW>(G);
 }
 
 template <int D>
 constexpr int kMinBlocks = D <= 128 ? 2 : 1;
 
-template <typename T, int D, int FEAT, int HPW>
-__global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(DecodeArgs a) {
-  constexpr bool SOFTCAP = FEAT & kSoftcap;
-  constexpr bool ALIBI = FEAT & kAlibi;
-  constexpr int KK = D / 32;   // QK mfma steps along D
-  constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
-  constexpr int NT = kNT<D, HPW>;
-  constexpr int KPS = 16 * NT; // keys per step
-  constexpr int P = kVPitch<D, HPW>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15;   // key row of the K piece / head column of the tile
-  const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
-
-  // Item order: split-major; within split p the (KV-head group, sequence)
-  // pairs are rotated by p groups.  Workgroup i runs on XCD i % 8 and, within
-  // it, on the shader engines in turn, so without the rotation all splits of
-  // a sequence would land on the same XCDs and engines and long sequences
-  // would load some of them more than others.
-  const int HG = a.Hkv / HPW;
-  const int per_split = HG * a.B;
-  const int split = blockIdx.x / per_split;
-  int j = blockIdx.x - split * per_split - static_cast<int>((int64_t)split * HG % per_split);
-  if (j < 0) j += per_split;
-  const int g0 = (j % HG) * HPW;  // first KV head of the item
-  const int b = j / HG;
-
-  const int L = a.seq_lens[b];
-  const int pos = L - 1;
+// Keys [lo, hi) of split p of a sequence of length L, and the first visible
+// one (sliding window); the split has work iff lo_vis < hi.
+struct SplitRange {
+  int lo, hi, lo_vis;
+};
+__device__ __forceinline__ SplitRange split_range(const DecodeArgs& a, int L, int p) {
+  SplitRange r;
   // split p covers keys [p * chunk, (p + 1) * chunk) of the sequence; the
   // last split also takes any keys past S * chunk
-  const int lo = static_cast<int>(min((int64_t)split * a.chunk, (int64_t)L));
-  const int hi = split == a.S - 1 ? L : min(lo + a.chunk, L);
-  const int lo_vis = a.window_left >= 0 ? max(lo, pos - a.window_left) : lo;
-  const int s_begin = lo_vis / KPS;
-  const int s_end = (hi + KPS - 1) / KPS;
-  const bool split_out = a.S > 1;
-  if (lo_vis >= hi) {
-    // no visible key: zero output, -inf log-sum-exp
-    for (int idx = threadIdx.x; idx < a.G * HPW * D; idx += kWaves * 64) {
-      const int h = g0 * a.G + idx / D;
-      const int d = idx % D;
-      if (split_out) {
-        a.part_out[(((int64_t)split * a.B + b) * a.Hq + h) * D + d] = 0.f;
-        if (d == 0) a.part_lse[((int64_t)split * a.Hq + h) * a.B + b] = kNegInf;
-      } else {
-        static_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + h) * D + d] = T::from_float(0.f);
-        if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.B + b] = kNegInf;
-      }
-    }
-    return;
-  }
+  r.lo = static_cast<int>(min((int64_t)p * a.chunk, (int64_t)L));
+  r.hi = p == a.S - 1 ? L : min(r.lo + a.chunk, L);
+  r.lo_vis = a.window_left >= 0 ? max(r.lo, L - 1 - a.window_left) : r.lo;
+  return r;
+}
 
-  const int GC = a.G * HPW;          // used columns
-  const int head = g0 * a.G + r16;  // query head of this lane's column
-  const bool col_ok = r16 < GC;
-  const int hsel = r16 / a.G;       // which of the item's KV heads the column reads
-  float slope_log2 = 0.0f;
-  if constexpr (ALIBI) slope_log2 = col_ok ? a.alibi[head] * kLog2e : 0.0f;
-
-  // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8; with
-  // two KV heads, operand h is zero outside head h's columns, so the two
-  // products accumulate into one S^T tile
-  v8s qf[HPW][KK];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + head) * D + c4 * 8;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-      const v8s qv = col_ok ? *reinterpret_cast<const v8s*>(qrow + kk * 32) : z;
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) qf[h][kk] = hsel == h ? qv : z;
-    }
-  }
-
-  const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
-  const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive slots
-  const uint16_t* kcg = a.kc + (int64_t)g0 * D + c4 * 8;
-  const uint16_t* vcg = a.vc + (int64_t)g0 * D + c4 * 8;
+// The pieces of one work item.
+template <typename T, int D, int FEAT, int HPW>
+struct Dec {
+  static constexpr bool SOFTCAP = FEAT & kSoftcap;
+  static constexpr bool ALIBI = FEAT & kAlibi;
+  static constexpr int KK = D / 32;   // QK mfma steps along D
+  static constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
+  static constexpr int NT = kNT<D, HPW>;
+  static constexpr int KPS = 16 * NT; // keys per step
+  static constexpr int P = kVPitch<D, HPW>;
+  static constexpr int CP = D + 4;    // combine row: m, l, 2 pad, O[D] (16-byte aligned)
 
   struct Frag {
     v8s k[HPW][NT][KK];
     v8s v[HPW][NT][KK];
   };
+
+  // KV heads g0 .. g0 + HPW - 1 of sequence b, keys [lo_vis, hi) of `split`
+  struct Item {
+    int g0, b, split;
+    int pos;             // the query's position, L - 1
+    int lo_vis, hi;
+    int s_begin, s_end;  // steps of KPS keys that cover [lo_vis, hi)
+    int last_j0;         // first key of the split's last tile of 16
+  };
+
+  static __device__ __forceinline__ Item make_item(const DecodeArgs& a, int g0, int b,
+                                                   int split, int L) {
+    Item it;
+    it.g0 = g0;
+    it.b = b;
+    it.split = split;
+    it.pos = L - 1;
+    const SplitRange r = split_range(a, L, split);
+    it.lo_vis = r.lo_vis;
+    it.hi = r.hi;
+    it.s_begin = r.lo_vis / KPS;
+    it.s_end = (r.hi + KPS - 1) / KPS;
+    it.last_j0 = r.hi > 0 ? ((r.hi - 1) & ~15) : 0;
+    return it;
+  }
+
   // Block ids of a step's tiles.  Loads are branch-free (so the compiler can
   // count outstanding loads exactly): a tile starting at or past hi is
   // clamped to the split's last tile, loaded, and fully masked.  The clamped
   // tile starts before hi, so it lies inside the sequence's last used block
   // at worst (block_size is a multiple of 16) and its block-table entry is
   // valid.
-  const int last_j0 = hi > 0 ? ((hi - 1) & ~15) : 0;
-  auto tile_j0 = [&](int step, int nt) { return min(step * KPS + 16 * nt, last_j0); };
-  auto fetch_ids = [&](int step, int (&ids)[NT]) {
+  static __device__ __forceinline__ int tile_j0(const Item& it, int step, int nt) {
+    return min(step * KPS + 16 * nt, it.last_j0);
+  }
+  static __device__ __forceinline__ void fetch_ids(const DecodeArgs& a, const Item& it, int step,
+                                                   int (&ids)[NT]) {
+    const int32_t* btab = a.block_table + (int64_t)it.b * a.bt_stride;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) ids[nt] = btab[div_magic(tile_j0(step, nt), a.bs_magic)];
-  };
-  auto load_step = [&](int step, const int (&ids)[NT], Frag& f) {
+    for (int nt = 0; nt < NT; ++nt) ids[nt] = btab[div_magic(tile_j0(it, step, nt), a.bs_magic)];
+  }
+  static __device__ __forceinline__ void load_step(const DecodeArgs& a, const Item& it, int step,
+                                                   const int (&ids)[NT], int r16, int c4,
+                                                   Frag& f) {
+    const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive slots
+    const uint16_t* kcg = a.kc + (int64_t)it.g0 * D + c4 * 8;
+    const uint16_t* vcg = a.vc + (int64_t)it.g0 * D + c4 * 8;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int j0 = tile_j0(step, nt);
+      const int j0 = tile_j0(it, step, nt);
       const int q = div_magic(j0, a.bs_magic);
       const int64_t slot = (int64_t)ids[nt] * a.bs + (j0 - q * a.bs) + r16;
       const uint16_t* kp = kcg + slot * row_stride;
@@ -195,17 +184,45 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
           f.v[h][nt][kk] = *reinterpret_cast<const v8s*>(vp + h * D + kk * 32);
         }
     }
-  };
+  }
 
-  float m_run = kNegInf;  // reference max (log2 units) of column r16
-  float l_run = 0.0f;     // this lane's share of the running sum
-  v4f o[DC];
+  // The Q row of this lane's column (head g0 * G + r16; padding columns load
+  // the item's first head and are masked by mask_q), without a branch.
+  static __device__ __forceinline__ void load_q(const DecodeArgs& a, const Item& it, int r16,
+                                                int c4, v8s (&qraw)[KK]) {
+    const int hq = it.g0 * a.G + (r16 < a.G * HPW ? r16 : 0);
+    const uint16_t* qrow = a.q + ((int64_t)it.b * a.Hq + hq) * D + c4 * 8;
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) o[dc] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const v8s*>(qrow + kk * 32);
+  }
+  // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8; with two
+  // KV heads, operand h is zero outside head h's columns, so the two products
+  // accumulate into one S^T tile
+  static __device__ __forceinline__ void mask_q(const v8s (&qraw)[KK], bool col_ok, int hsel,
+                                                v8s (&qf)[HPW][KK]) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) qf[h][kk] = (col_ok && hsel == h) ? qraw[kk] : z;
+    }
+  }
+  // ALiBi slope of this lane's column, in log2 units
+  static __device__ __forceinline__ float slope_of(const DecodeArgs& a, const Item& it, int r16) {
+    if constexpr (ALIBI)
+      return r16 < a.G * HPW ? a.alibi[it.g0 * a.G + r16] * kLog2e : 0.0f;
+    else
+      return 0.0f;
+  }
 
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * KPS * P;
-
-  auto compute_step = [&](int step, const Frag& f) {
+  // One step of KPS keys: scores, online softmax, P.V.  m_run is the
+  // reference max (log2 units) of column r16, l_run this lane's share of the
+  // running sum, o the lane's O^T[d = dc*16 + 4*c4 + e][head r16].
+  static __device__ __forceinline__ void compute_step(const DecodeArgs& a, const Item& it,
+                                                      int step, const Frag& f,
+                                                      const v8s (&qf)[HPW][KK], float slope_log2,
+                                                      int r16, int c4, int hsel, uint16_t* vs,
+                                                      float& m_run, float& l_run, v4f (&o)[DC]) {
     float x[NT][4];
     float mx = kNegInf;
 #pragma unroll
@@ -223,8 +240,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
         float v;
         if constexpr (SOFTCAP) v = a.cap_log2 * tanh_f32(sc[e] * a.scale_over_cap);
         else v = sc[e] * a.scale_log2;
-        if constexpr (ALIBI) v -= slope_log2 * static_cast<float>(pos - key);
-        x[nt][e] = (key >= lo_vis && key < hi) ? v : kNegInf;
+        if constexpr (ALIBI) v -= slope_log2 * static_cast<float>(it.pos - key);
+        x[nt][e] = (key >= it.lo_vis && key < it.hi) ? v : kNegInf;
         mx = fmaxf(mx, x[nt][e]);
       }
     }
@@ -260,7 +277,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int key = step * KPS + 16 * nt + r16;
-      const bool row_ok = key >= lo_vis && key < hi;
+      const bool row_ok = key >= it.lo_vis && key < it.hi;
       uint16_t* dst = vs + (16 * nt + r16) * P + c4 * 8;
 #pragma unroll
       for (int h = 0; h < HPW; ++h)
@@ -280,9 +297,9 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
       const v8s pb = __builtin_bit_cast(v8s, pq);
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const v4s lo = lds_read_tr16(vb + dc * 16);
-        const v4s hi = lds_read_tr16(vb + 16 * P + dc * 16);
-        const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const v4s v0 = lds_read_tr16(vb + dc * 16);
+        const v4s v1 = lds_read_tr16(vb + 16 * P + dc * 16);
+        const v8s av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         o[dc] = T::mfma16x16x32(av, pb, o[dc]);
       }
     } else {
@@ -300,84 +317,154 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
       }
     }
     wave_lds_sync();
-  };
+  }
+
+  // Result of column j (query head g0 * G + j), elements d .. d + 3.
+  static __device__ __forceinline__ void emit4(const DecodeArgs& a, int g0, int b, int split,
+                                               int j, int d, v4f val, float lse) {
+    const int h = g0 * a.G + j;
+    if (a.S > 1) {
+      *reinterpret_cast<v4f*>(a.part_out + (((int64_t)split * a.B + b) * a.Hq + h) * D + d) = val;
+      if (d == 0) a.part_lse[((int64_t)split * a.Hq + h) * a.B + b] = lse;
+    } else {
+      const u32x2 w = {T::pack2(val[0], val[1]), T::pack2(val[2], val[3])};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + h) * D + d) = w;
+      if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.B + b] = lse;
+    }
+  }
+  // An item without visible keys: zero output, -inf log-sum-exp.
+  static __device__ __forceinline__ void emit_empty(const DecodeArgs& a, int g0, int b,
+                                                    int split) {
+    for (int idx = threadIdx.x; idx < a.G * HPW * (D / 4); idx += kWaves * 64) {
+      const int j = idx / (D / 4);
+      emit4(a, g0, b, split, j, (idx - j * (D / 4)) * 4, v4f{0.f, 0.f, 0.f, 0.f}, kNegInf);
+    }
+  }
+
+  // Merge the waves' states of an item through LDS (comb) and write its
+  // result.  Starts with a barrier: every wave is done with the item (and
+  // with its V slab, which comb may reuse) and with the previous item's
+  // combine.
+  static __device__ __forceinline__ void combine_emit(const DecodeArgs& a, const Item& it,
+                                                      int wave, int r16, int c4, float m_run,
+                                                      float l_run, const v4f (&o)[DC],
+                                                      float* comb) {
+    const int GC = a.G * HPW;
+    float l_tot = l_run + shfl_xor(l_run, 16);
+    l_tot += shfl_xor(l_tot, 32);
+    __syncthreads();
+    if (r16 < GC) {
+      float* row = comb + (wave * GC + r16) * CP;
+      if (c4 == 0) *reinterpret_cast<f2*>(row) = f2{m_run, l_tot};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) *reinterpret_cast<v4f*>(row + 4 + dc * 16 + 4 * c4) = o[dc];
+    }
+    __syncthreads();
+    // four consecutive elements per thread and pass
+    for (int idx = threadIdx.x; idx < GC * (D / 4); idx += kWaves * 64) {
+      const int j = idx / (D / 4);
+      const int d = (idx - j * (D / 4)) * 4;
+      f2 ml[kWaves];
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        ml[w] = *reinterpret_cast<const f2*>(comb + (w * GC + j) * CP);
+        M = fmaxf(M, ml[w][0]);
+      }
+      v4f num = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float fw = fast_exp2(ml[w][0] - M);
+          den += fw * ml[w][1];
+          num += fw * *reinterpret_cast<const v4f*>(comb + (w * GC + j) * CP + 4 + d);
+        }
+      }
+      const float inv = den > 0.f ? 1.0f / den : 0.f;
+      const float lse = den > 0.f ? (M + __log2f(den)) * kLn2 : kNegInf;
+      emit4(a, it.g0, it.b, it.split, j, d, num * inv, lse);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// One work item per workgroup.
+// Item order: split-major; within split p the (KV-head group, sequence) pairs
+// are rotated by p groups.  Workgroup i runs on XCD i % 8 and, within it, on
+// the shader engines in turn, so without the rotation all splits of a
+// sequence would land on the same XCDs and engines and long sequences would
+// load some of them more than others.
+template <typename T, int D, int FEAT, int HPW>
+__global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(DecodeArgs a) {
+  using K = Dec<T, D, FEAT, HPW>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;   // key row of the K piece / head column of the tile
+  const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
+
+  const int HG = a.Hkv / HPW;
+  const int per_split = HG * a.B;
+  const int split = blockIdx.x / per_split;
+  int j = blockIdx.x - split * per_split - static_cast<int>((int64_t)split * HG % per_split);
+  if (j < 0) j += per_split;
+  const int g0 = (j % HG) * HPW;  // first KV head of the item
+  const int b = j / HG;
+
+  const typename K::Item it = K::make_item(a, g0, b, split, a.seq_lens[b]);
+  if (it.lo_vis >= it.hi) {
+    K::emit_empty(a, g0, b, split);
+    return;
+  }
+  const bool col_ok = r16 < a.G * HPW;
+  const int hsel = r16 / a.G;  // which of the item's KV heads the column reads
+  const float slope_log2 = K::slope_of(a, it, r16);
+
+  v8s qraw[K::KK];
+  K::load_q(a, it, r16, c4, qraw);
+
+  float m_run = kNegInf;
+  float l_run = 0.0f;
+  v4f o[K::DC];
+#pragma unroll
+  for (int dc = 0; dc < K::DC; ++dc) o[dc] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * K::KPS * K::P;
 
   // ---- double buffer: the next step's loads are in flight while the
   //      current one is computed.  Block ids run one step further ahead and
   //      are issued before the K/V loads, so waiting for them never waits for
   //      K/V data (the vector-memory counter completes in issue order).
-  Frag cur, nxt;
-  int ids[NT];
-  int step = s_begin + wave;
-  if (step < s_end) {
-    fetch_ids(step, ids);
-    load_step(step, ids, cur);
-    fetch_ids(min(step + kWaves, s_end - 1), ids);
+  typename K::Frag cur, nxt;
+  int ids[K::NT];
+  int step = it.s_begin + wave;
+  if (step < it.s_end) {
+    K::fetch_ids(a, it, step, ids);
+    K::load_step(a, it, step, ids, r16, c4, cur);
+    K::fetch_ids(a, it, min(step + kWaves, it.s_end - 1), ids);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first step landed
-  for (; step < s_end; step += kWaves) {
-    if (step + kWaves < s_end) {
-      int ids2[NT];
-      fetch_ids(min(step + 2 * kWaves, s_end - 1), ids2);
-      load_step(step + kWaves, ids, nxt);
+  v8s qf[HPW][K::KK];
+  K::mask_q(qraw, col_ok, hsel, qf);
+  for (; step < it.s_end; step += kWaves) {
+    if (step + kWaves < it.s_end) {
+      int ids2[K::NT];
+      K::fetch_ids(a, it, min(step + 2 * kWaves, it.s_end - 1), ids2);
+      K::load_step(a, it, step + kWaves, ids, r16, c4, nxt);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) ids[nt] = ids2[nt];
+      for (int nt = 0; nt < K::NT; ++nt) ids[nt] = ids2[nt];
     }
-    compute_step(step, cur);
+    K::compute_step(a, it, step, cur, qf, slope_log2, r16, c4, hsel, vs, m_run, l_run, o);
     cur = nxt;
   }
-
-  // ---- combine the waves: lane holds O^T[d = dc*16 + 4*c4 + e][head r16]
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
-  __syncthreads();  // every wave is done with its V slab
-  float* comb = reinterpret_cast<float*>(smem);  // [wave][GC][D + 2]: m, l, O[D]
-  constexpr int CP = D + 2;
-  if (col_ok) {
-    float* row = comb + (wave * GC + r16) * CP;
-    if (c4 == 0) {
-      row[0] = m_run;
-      row[1] = l_tot;
-    }
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) row[2 + dc * 16 + 4 * c4 + e] = o[dc][e];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GC * D; idx += kWaves * 64) {
-    const int j = idx / D;
-    const int d = idx - j * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb[(w * GC + j) * CP]);
-    float num = 0.f, den = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* row = comb + (w * GC + j) * CP;
-        const float fw = fast_exp2(row[0] - M);
-        den += fw * row[1];
-        num += fw * row[2 + d];
-      }
-    }
-    const float val = den > 0.f ? num / den : 0.f;
-    const int h = g0 * a.G + j;
-    const float lse = den > 0.f ? (M + __log2f(den)) * kLn2 : kNegInf;
-    if (split_out) {
-      a.part_out[(((int64_t)split * a.B + b) * a.Hq + h) * D + d] = val;
-      if (d == 0) a.part_lse[((int64_t)split * a.Hq + h) * a.B + b] = lse;
-    } else {
-      static_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + h) * D + d] = T::from_float(val);
-      if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.B + b] = lse;
-    }
-  }
+  K::combine_emit(a, it, wave, r16, c4, m_run, l_run, o, reinterpret_cast<float*>(smem));
 }
 
 template <typename T, int D, int FEAT, int HPW>
 int launch_h(const DecodeArgs& args, hipStream_t stream) {
-  const int64_t grid = (int64_t)(args.Hkv / HPW) * args.B * args.S;
-  hipLaunchKernelGGL((decode_kernel<T, D, FEAT, HPW>), dim3(static_cast<unsigned>(grid)),
+  const int64_t items = (int64_t)(args.Hkv / HPW) * args.B * args.S;
+  hipLaunchKernelGGL((decode_kernel<T, D, FEAT, HPW>), dim3(static_cast<unsigned>(items)),
                      dim3(kWaves * 64), (decode_lds_bytes<D, HPW>(args.G)), stream, args);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
