@@ -245,7 +245,7 @@ def prefill_batch(seed: int = 3) -> Workload:
     return w
 
 
-def mixed_batch(seed: int = 4, num_splits: int = 4) -> Workload:
+def mixed_batch(seed: int = 4, num_splits: int = 16) -> Workload:
     """bf16 mixed chunked-prefill: 48 decode sequences (context uniform in
     [1024, 8192]) and 4 prefill chunks of 512 new tokens on contexts uniform
     in [2048, 8192]; 32 query / 8 KV heads of size 128, block 32, sliding
