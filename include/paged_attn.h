@@ -22,7 +22,8 @@
  *    written.  pa_last_error() gives a message for the last failure of the
  *    calling thread.
  *  - Contents of device arrays (slot ids, block ids, lengths) are trusted:
- *    an out-of-range block id or slot is undefined behaviour.
+ *    an out-of-range block id or slot is undefined behaviour
+ *    (pa_check_indices counts such entries, for tests and debugging).
  *  - dtype of q / key / value / caches / out: PA_F16 or PA_BF16.  All
  *    arithmetic is fp32; outputs are rounded to nearest-even.
  *  - head_size must be 64, 128 or 256; block_size a positive multiple of 16
@@ -175,6 +176,34 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
                       int64_t num_tokens, int num_heads, int head_size,
                       pa_dtype_t parts_dtype, pa_dtype_t out_dtype,
                       void* stream);
+
+/*
+ * pa_check_indices — debug validation of the device index arrays that the
+ * calls above trust (their contents are undefined behaviour when out of
+ * range).  Optional, for tests and debugging; not on the hot path.
+ * [vLLM flash_attn.py (e2f56c3), FlashAttentionImpl.forward: slot_mapping
+ * addresses cache slots, block_table maps each sequence's logical blocks;
+ * Aphrodite flash_attn.py, FlashAttentionMetadata, block_tables.]
+ *
+ *   slot_mapping    int64 [num_tokens] or NULL when num_tokens == 0.
+ *   block_table     int32 rows of block_table_stride entries, one per
+ *                   sequence; seq_lens int32 [num_seqs].  Both may be NULL
+ *                   when num_seqs == 0.
+ *   counts          int32 [3], device, caller-owned; overwritten with
+ *     counts[0]  slots >= num_blocks * block_size (negative slots are
+ *                padding and allowed);
+ *     counts[1]  block ids outside [0, num_blocks) among the entries a call
+ *                reads: the first ceil(seq_lens[b] / block_size) of row b
+ *                (padding past them is not looked at);
+ *     counts[2]  sequences with a negative length, or with more blocks than
+ *                a row holds (their rows are not read).
+ *   Enqueued on `stream` like the other calls; read counts after it.
+ *   block_size a positive multiple of 16; num_blocks > 0.
+ */
+int pa_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
+                     const int32_t* block_table, int64_t block_table_stride,
+                     const int32_t* seq_lens, int num_seqs, int64_t num_blocks,
+                     int block_size, int32_t* counts, void* stream);
 
 /* Message describing the last non-OK return on the calling thread ("" if
  * none).  The string is owned by the library and valid until the next call

@@ -4,8 +4,8 @@ Every function here only marshals arguments (torch tensors -> device
 pointers and sizes, the current HIP stream) and calls the entry point of the
 same name in ``libpagedattn.so`` (declared in ``include/paged_attn.h``).  All
 work runs in the library's HIP kernels; there is no fallback.  Importing the
-package fails if the library has not been built (``python -m
-paged_kv_attention_29_amd.build`` or ``__graft_entry__.build()``).
+package fails if the library has not been built (``python
+paged_kv_attention_29_amd/build.py`` or ``__graft_entry__.build()``).
 
 Tensors are caller-owned and must live on the GPU; the library allocates
 nothing.  Shapes follow the C header:
@@ -29,6 +29,7 @@ __all__ = [
     "paged_attn_prefill",
     "paged_attn_decode",
     "merge_attn_states",
+    "check_indices",
     "pa_last_error",
     "library_path",
 ]
@@ -51,7 +52,7 @@ class PagedAttnError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(library_path):
         raise ImportError(
-            f"{library_path} is missing: build it with `python -m paged_kv_attention_29_amd.build`")
+            f"{library_path} is missing: build it with `python paged_kv_attention_29_amd/build.py`")
     lib = ctypes.CDLL(library_path)
     lib.reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                                       _i32, _i32, _vp]
@@ -62,7 +63,9 @@ def _load() -> ctypes.CDLL:
                                       _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
                                       _i32, _i32, _vp]
     lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
-    for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states"):
+    lib.pa_check_indices.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i32, _vp, _vp]
+    for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states",
+               "pa_check_indices"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -155,3 +158,21 @@ def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: tor
         _ptr(out), _ptr(out_lse), _ptr(parts_out), _ptr(parts_lse), s, t, h, d,
         _code(parts_out.dtype), _code(out.dtype), _stream(stream)))
     return out
+
+
+def check_indices(num_blocks: int, block_size: int, slot_mapping: Optional[torch.Tensor] = None,
+                  block_table: Optional[torch.Tensor] = None,
+                  seq_lens: Optional[torch.Tensor] = None,
+                  counts: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Counts of out-of-range slots, block ids a call would read, and bad
+    sequence lengths (int32 [3] on the GPU; see pa_check_indices)."""
+    if counts is None:
+        dev = next(t for t in (slot_mapping, block_table, seq_lens) if t is not None).device
+        counts = torch.empty(3, dtype=torch.int32, device=dev)
+    n_tok = 0 if slot_mapping is None else slot_mapping.numel()
+    n_seq = 0 if seq_lens is None else seq_lens.numel()
+    stride = 0 if block_table is None else block_table.stride(0)
+    _check("pa_check_indices", lib.pa_check_indices(
+        _ptr(slot_mapping), n_tok, _ptr(block_table), stride, _ptr(seq_lens), n_seq,
+        int(num_blocks), int(block_size), _ptr(counts), _stream(stream)))
+    return counts

@@ -246,4 +246,26 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out, const fl
                     fn);
 }
 
+int pa_check_indices(const int64_t* slot_mapping, int64_t num_tokens, const int32_t* block_table,
+                     int64_t block_table_stride, const int32_t* seq_lens, int num_seqs,
+                     int64_t num_blocks, int block_size, int32_t* counts, void* stream) {
+  const char* fn = "pa_check_indices";
+  if (counts == nullptr) return fail(PA_ERR_INVALID, "%s: NULL counts", fn);
+  if (block_size <= 0 || block_size % 16 != 0)
+    return fail(PA_ERR_INVALID, "%s: block_size must be a positive multiple of 16 (got %d)", fn,
+                block_size);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
+  if (num_tokens < 0 || num_seqs < 0)
+    return fail(PA_ERR_INVALID, "%s: num_tokens and num_seqs must be >= 0", fn);
+  if (num_tokens > 0 && slot_mapping == nullptr)
+    return fail(PA_ERR_INVALID, "%s: NULL slot_mapping", fn);
+  if (num_seqs > 0 && (block_table == nullptr || seq_lens == nullptr || block_table_stride <= 0))
+    return fail(PA_ERR_INVALID, "%s: num_seqs > 0 needs block_table, seq_lens and a positive stride",
+                fn);
+  return hip_result(pa::launch_check_indices(slot_mapping, num_tokens, block_table,
+                                             block_table_stride, seq_lens, num_seqs, num_blocks,
+                                             block_size, counts, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

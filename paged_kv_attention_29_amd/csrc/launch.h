@@ -48,6 +48,11 @@ struct AttnParams {
 };
 
 int launch_decode(const AttnParams& p, hipStream_t stream);
+
+int launch_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                         int num_seqs, int64_t num_blocks, int block_size, int32_t* counts,
+                         hipStream_t stream);
 int launch_prefill(const AttnParams& p, hipStream_t stream);
 
 }  // namespace pa

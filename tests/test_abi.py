@@ -100,3 +100,16 @@ def test_merge_validation(lib):
     assert f(1, None, 1, 1, 2, 4, 2, 64, 9, lib.PA_BF16, None) == -2
     assert f(None, None, 1, 1, 2, 4, 2, 64, lib.PA_F32, lib.PA_BF16, None) == -1
     assert f(None, None, None, None, 2, 0, 2, 64, lib.PA_F32, lib.PA_BF16, None) == 0
+
+
+def test_check_indices_validation(lib):
+    f = lib.lib.pa_check_indices
+    # (slots, n_tok, table, stride, lens, n_seq, num_blocks, block_size, counts, stream)
+    assert f(1, 4, 1, 8, 1, 2, 10, 16, None, None) == -1          # no counts buffer
+    assert f(1, 4, 1, 8, 1, 2, 10, 24, 1, None) == -1             # block size
+    assert f(1, 4, 1, 8, 1, 2, 0, 16, 1, None) == -1              # no blocks
+    assert f(None, 4, 1, 8, 1, 2, 10, 16, 1, None) == -1          # slots missing
+    assert f(1, 4, None, 8, 1, 2, 10, 16, 1, None) == -1          # table missing
+    assert f(1, 4, 1, 0, 1, 2, 10, 16, 1, None) == -1             # stride
+    assert f(1, -1, 1, 8, 1, 2, 10, 16, 1, None) == -1
+    assert lib.pa_last_error().startswith("pa_check_indices")

@@ -107,7 +107,7 @@ def test_lds_dma_waits_after_m0_write(prefill_asm):
     assert n_dma > 0
 
 
-@pytest.mark.parametrize("src", ["prefill.hip", "decode.hip", "merge.hip", "reshape_and_cache.hip"])
+@pytest.mark.parametrize("src", sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")))
 def test_no_scalar_cache_writes(src, tmp_path):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
