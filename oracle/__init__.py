@@ -16,6 +16,8 @@ mathematics independent of this code:
                         (float64) with hand-built masks; closed forms.
 * ``decode_splits``  — split-then-merge equals the unsplit result.
 * ``merge``          — closed forms (identical states, -inf parts).
+* ``cascade``        — equals plain causal ``attend`` (itself pinned above)
+                        on batches that share a block-aligned prefix.
 
 Readings the pages leave open (softcap/ALiBi order, ALiBi slope index,
 window edge) are fixed by the readings documented with each function; they
@@ -30,6 +32,7 @@ from .paged_attention import (
     split_bounds,
     decode_splits,
     merge,
+    cascade,
 )
 
 __all__ = [
@@ -40,4 +43,5 @@ __all__ = [
     "split_bounds",
     "decode_splits",
     "merge",
+    "cascade",
 ]

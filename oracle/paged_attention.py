@@ -250,3 +250,39 @@ def merge(parts_out: torch.Tensor, parts_lse: torch.Tensor):
     lse = torch.where(finite, Msafe + torch.log(torch.where(finite, wsum, torch.ones_like(wsum))),
                       torch.full_like(M, _NEG_INF))
     return out, lse
+
+
+def cascade(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+            cu_seqlens_q: Sequence[int], seq_lens: Sequence[int], block_table: torch.Tensor,
+            scale: float, common_prefix_len: int, softcap: float = 0.0):
+    """Causal varlen attention of a batch whose sequences share their first
+    common_prefix_len keys, taken the cascade way [vLLM flash_attn.py
+    (e2f56c3), cascade_attention]:
+
+    1. every query of the batch against the shared prefix keys, as one
+       sequence of all the queries over block_table[:1], non-causal (the
+       queries all come after the prefix, so none of its keys is masked);
+    2. each sequence's queries against the keys after the prefix, causal,
+       with seq_lens - common_prefix_len keys through
+       block_table[:, common_prefix_len / block_size:];
+    3. the two partial states merged by their log-sum-exp (``merge``).
+
+    The page asserts no ALiBi and no sliding window for it, a prefix that is
+    a positive multiple of the block size, and (implicitly) that every
+    query comes after the prefix; those preconditions are asserted here.
+    Returns (out, lse) like ``attend``.
+    """
+    block_size = key_cache.shape[1]
+    assert common_prefix_len > 0 and common_prefix_len % block_size == 0
+    n = common_prefix_len // block_size
+    total_q = q.shape[0]
+    for b in range(len(seq_lens)):
+        q_len = int(cu_seqlens_q[b + 1]) - int(cu_seqlens_q[b])
+        assert int(seq_lens[b]) - q_len >= common_prefix_len, "queries must follow the prefix"
+        assert torch.equal(block_table[b, :n], block_table[0, :n]), "prefix blocks must be shared"
+    pre_out, pre_lse = attend(q, key_cache, value_cache, [0, total_q], [common_prefix_len],
+                              block_table[:1], scale, causal=False, softcap=softcap)
+    suf_out, suf_lse = attend(q, key_cache, value_cache, cu_seqlens_q,
+                              [int(L) - common_prefix_len for L in seq_lens], block_table[:, n:],
+                              scale, causal=True, softcap=softcap)
+    return merge(torch.stack([pre_out, suf_out]), torch.stack([pre_lse, suf_lse]))

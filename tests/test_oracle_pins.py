@@ -413,3 +413,52 @@ def test_merge_two_parts_matches_softmax_over_union():
     s = torch.cat([s1, s2])
     assert torch.allclose(mo[0, 0], torch.softmax(s, 0) @ torch.cat([v1, v2]), atol=1e-14)
     assert abs(float(ml[0, 0]) - float(torch.logsumexp(s, 0))) < 1e-14
+
+
+def _shared_prefix_case(seed, B, P, q_lens, extra, Hq, Hkv, D, bs):
+    """A cache whose sequences share their first P keys (same physical
+    blocks), random K/V in every block, and queries after the prefix."""
+    g = torch.Generator().manual_seed(seed)
+    n = P // bs
+    lens = [P + e + ql for e, ql in zip(extra, q_lens)]
+    own = [-(-(L - P) // bs) for L in lens]
+    nb = n + sum(own) + 2
+    perm = torch.randperm(nb, generator=g)
+    table = torch.zeros(B, n + max(own), dtype=torch.int32)
+    table[:, :n] = perm[:n]
+    at = n
+    for b in range(B):
+        table[b, n:n + own[b]] = perm[at:at + own[b]]
+        at += own[b]
+    kc = torch.randn(nb, bs, Hkv, D, generator=g)
+    vc = torch.randn(nb, bs, Hkv, D, generator=g)
+    cu = [0]
+    for ql in q_lens:
+        cu.append(cu[-1] + ql)
+    q = torch.randn(cu[-1], Hq, D, generator=g)
+    return q, kc, vc, cu, lens, table
+
+
+@pytest.mark.parametrize("cap", [0.0, 3.0])
+def test_cascade_equals_plain_causal(cap):
+    """The cascade decomposition (shared prefix non-causal, suffix causal,
+    LSE merge) reproduces plain causal attention."""
+    q, kc, vc, cu, lens, table = _shared_prefix_case(9, 5, 48, [1, 7, 3, 16, 2], [0, 5, 17, 40, 1],
+                                                     8, 2, 16, 16)
+    o, l = oracle.cascade(q, kc, vc, cu, lens, table, 0.3, 48, softcap=cap)
+    ro, rl = oracle.attend(q, kc, vc, cu, lens, table, 0.3, True, -1, cap, None)
+    assert torch.allclose(o, ro, atol=1e-12, rtol=0) and torch.allclose(l, rl, atol=1e-12, rtol=0)
+
+
+def test_cascade_matches_brute_force_tiny():
+    q, kc, vc, cu, lens, table = _shared_prefix_case(10, 3, 16, [2, 1, 3], [1, 0, 2], 4, 2, 8, 16)
+    o, l = oracle.cascade(q, kc, vc, cu, lens, table, 0.5, 16)
+    bo, bl = brute_force(q, kc, vc, cu, lens, table, 0.5, True, -1, 0.0, None)
+    assert torch.allclose(o, bo, atol=1e-12, rtol=0) and torch.allclose(l, bl, atol=1e-12, rtol=0)
+
+
+def test_cascade_rejects_unshared_prefix():
+    q, kc, vc, cu, lens, table = _shared_prefix_case(11, 2, 32, [1, 1], [0, 0], 4, 2, 8, 16)
+    table[1, 0] = table[1, 0] + 100
+    with pytest.raises(AssertionError):
+        oracle.cascade(q, kc, vc, cu, lens, table, 0.5, 32)
