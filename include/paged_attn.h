@@ -178,6 +178,48 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
                       void* stream);
 
 /*
+ * paged_attn_cascade — causal prefill of a batch whose sequences share their
+ * first common_prefix_len keys, computed the cascade way [vLLM flash_attn.py
+ * (e2f56c3), cascade_attention]: every query against the shared prefix once
+ * (non-causal, through block_table row 0), each sequence's queries against
+ * its own keys after the prefix (causal, through the rest of its row), and
+ * the log-sum-exp merge of the two.  The result equals paged_attn_prefill
+ * with causal = 1 on the same batch; the shared prefix is read once for the
+ * batch rather than once per sequence.
+ *
+ *   Arguments as for paged_attn_prefill (causal, no window, no ALiBi: the
+ *   page's cascade supports neither), plus
+ *   common_prefix_len  > 0, a multiple of block_size, below max_seqlen_k.
+ *                      The caller guarantees (device data, not checked):
+ *                      the first common_prefix_len / block_size entries of
+ *                      every block-table row are the same blocks, and every
+ *                      sequence's queries come after the prefix
+ *                      (seq_len - query_len >= common_prefix_len).
+ *   max_prefix_splits  1..255: the prefix pass may split the prefix keys
+ *                      into up to this many parts (it does when there are
+ *                      few queries, as in a decode batch, so that the pass
+ *                      fills the GPU); the workspaces hold that many parts
+ *                      plus one;
+ *   parts_out          workspace [max_prefix_splits + 1, total_q, num_heads,
+ *                      head_size] of dtype (prefix parts, then the suffix);
+ *   parts_lse          fp32 workspace [max_prefix_splits + 1, num_heads,
+ *                      total_q];
+ *   work_ints          int32 workspace [num_seqs + 3].
+ *   Workspaces are caller-owned and overwritten; num_kv_heads * total_q must
+ *   be below 2^31.
+ */
+int paged_attn_cascade(void* out, float* lse, const void* q,
+                       const void* key_cache, const void* value_cache,
+                       const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                       const int32_t* block_table, int64_t block_table_stride,
+                       int num_seqs, int64_t total_q, int max_seqlen_q,
+                       int max_seqlen_k, int num_heads, int num_kv_heads,
+                       int head_size, int block_size, int64_t num_blocks,
+                       float scale, float softcap, int common_prefix_len,
+                       int max_prefix_splits, void* parts_out, float* parts_lse,
+                       int32_t* work_ints, pa_dtype_t dtype, void* stream);
+
+/*
  * pa_check_indices — debug validation of the device index arrays that the
  * calls above trust (their contents are undefined behaviour when out of
  * range).  Optional, for tests and debugging; not on the hot path.

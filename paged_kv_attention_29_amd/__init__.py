@@ -29,6 +29,7 @@ __all__ = [
     "paged_attn_prefill",
     "paged_attn_decode",
     "merge_attn_states",
+    "paged_attn_cascade",
     "check_indices",
     "pa_last_error",
     "library_path",
@@ -64,8 +65,11 @@ def _load() -> ctypes.CDLL:
                                       _i32, _i32, _vp]
     lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
     lib.pa_check_indices.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i32, _vp, _vp]
+    lib.paged_attn_cascade.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _i32,
+                                       _i32, _vp, _vp, _vp, _i32, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states",
-               "pa_check_indices"):
+               "pa_check_indices", "paged_attn_cascade"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -158,6 +162,34 @@ def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: tor
         _ptr(out), _ptr(out_lse), _ptr(parts_out), _ptr(parts_lse), s, t, h, d,
         _code(parts_out.dtype), _code(out.dtype), _stream(stream)))
     return out
+
+
+def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                       seq_lens: torch.Tensor, block_table: torch.Tensor, max_seqlen_q: int,
+                       max_seqlen_k: int, scale: float, common_prefix_len: int,
+                       softcap: float = 0.0, lse: Optional[torch.Tensor] = None,
+                       max_prefix_splits: int = 16, workspace=None, stream=None) -> None:
+    """Causal prefill over a shared prefix (see paged_attn_cascade in the
+    header).  ``workspace`` is (parts_out, parts_lse, work_ints) sized for
+    max_prefix_splits + 1 parts; it is allocated here with torch when not
+    given."""
+    t, hq, d = q.shape
+    nb, bs, hkv, _ = key_cache.shape
+    b = seq_lens.numel()
+    if workspace is None:
+        n = max_prefix_splits + 1
+        workspace = (torch.empty(n, t, hq, d, dtype=q.dtype, device=q.device),
+                     torch.empty(n, hq, t, dtype=torch.float32, device=q.device),
+                     torch.empty(b + 3, dtype=torch.int32, device=q.device))
+    parts_out, parts_lse, ints = workspace
+    _check("paged_attn_cascade", lib.paged_attn_cascade(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
+        _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b, t, int(max_seqlen_q),
+        int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), float(softcap),
+        int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), _ptr(ints),
+        _code(q.dtype),
+        _stream(stream)))
 
 
 def check_indices(num_blocks: int, block_size: int, slot_mapping: Optional[torch.Tensor] = None,

@@ -246,6 +246,76 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out, const fl
                     fn);
 }
 
+int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cache,
+                       const void* value_cache, const int32_t* cu_seqlens_q,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int64_t block_table_stride, int num_seqs, int64_t total_q,
+                       int max_seqlen_q, int max_seqlen_k, int num_heads, int num_kv_heads,
+                       int head_size, int block_size, int64_t num_blocks, float scale,
+                       float softcap, int common_prefix_len, int max_prefix_splits,
+                       void* parts_out, float* parts_lse, int32_t* work_ints, pa_dtype_t dtype,
+                       void* stream) {
+  const char* fn = "paged_attn_cascade";
+  int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, scale, -1, softcap, dtype, q, key_cache, value_cache,
+                             seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
+  if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(PA_ERR_INVALID, "%s: total_q / max_seqlen_q / max_seqlen_k must be >= 0", fn);
+  if (common_prefix_len <= 0 || common_prefix_len % block_size != 0)
+    return fail(PA_ERR_INVALID,
+                "%s: common_prefix_len must be a positive multiple of block_size (got %d)", fn,
+                common_prefix_len);
+  if (common_prefix_len >= max_seqlen_k && num_seqs > 0)
+    return fail(PA_ERR_INVALID, "%s: common_prefix_len (%d) must be below max_seqlen_k (%d)", fn,
+                common_prefix_len, max_seqlen_k);
+  if (max_prefix_splits < 1 || max_prefix_splits > 255)
+    return fail(PA_ERR_INVALID, "%s: max_prefix_splits must be in [1, 255] (got %d)", fn,
+                max_prefix_splits);
+  if (num_seqs > 0 && (cu_seqlens_q == nullptr || parts_out == nullptr || parts_lse == nullptr ||
+                       work_ints == nullptr))
+    return fail(PA_ERR_INVALID, "%s: NULL cu_seqlens_q or workspace", fn);
+  if (num_heads / num_kv_heads > 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 128 query heads per KV head", fn);
+  if (max_seqlen_k >= (1 << 24))
+    return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
+  if (num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 sequences in one call", fn);
+  // the prefix pass takes every query as one sequence
+  if ((int64_t)num_kv_heads * total_q > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads * total_q must be below 2^31", fn);
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  pa::AttnParams p{};
+  p.out = out;
+  p.lse = lse;
+  p.q = q;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.block_table_stride = block_table_stride;
+  p.num_seqs = num_seqs;
+  p.total_q = total_q;
+  p.max_seqlen_q = max_seqlen_q;
+  p.max_seqlen_k = max_seqlen_k;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_size = head_size;
+  p.block_size = block_size;
+  p.scale = scale;
+  p.causal = 1;
+  p.window_left = -1;
+  p.softcap = softcap;
+  p.alibi_slopes = nullptr;
+  p.num_splits = 1;
+  p.dtype = static_cast<pa::Dtype>(dtype);
+  return hip_result(pa::launch_cascade(p, common_prefix_len, max_prefix_splits, parts_out,
+                                       parts_lse, work_ints, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int pa_check_indices(const int64_t* slot_mapping, int64_t num_tokens, const int32_t* block_table,
                      int64_t block_table_stride, const int32_t* seq_lens, int num_seqs,
                      int64_t num_blocks, int block_size, int32_t* counts, void* stream) {

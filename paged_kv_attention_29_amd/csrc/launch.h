@@ -44,6 +44,7 @@ struct AttnParams {
   float softcap;
   const float* alibi_slopes;
   int num_splits;
+  int key_split;  // prefill only: keys per split (a multiple of 64), 0 = none
   Dtype dtype;
 };
 
@@ -54,5 +55,10 @@ int launch_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
                          int num_seqs, int64_t num_blocks, int block_size, int32_t* counts,
                          hipStream_t stream);
 int launch_prefill(const AttnParams& p, hipStream_t stream);
+// prefix-shared causal prefill (p.causal, no window / ALiBi): parts_out
+// [max_prefix_splits + 1, T, Hq, D] in p.dtype, parts_lse
+// [max_prefix_splits + 1, Hq, T], ints [num_seqs + 3]
+int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void* parts_out,
+                   float* parts_lse, int32_t* ints, hipStream_t stream);
 
 }  // namespace pa

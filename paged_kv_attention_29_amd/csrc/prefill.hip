@@ -69,6 +69,10 @@ struct PrefillArgs {
   float cap_log2;       // softcap * log2(e)
   int causal, window_left;
   const float* alibi;
+  // key splits (grid z): split z takes keys [z * key_split, (z + 1) * key_split)
+  // and writes its normalised partial result and LSE as part z of out / lse
+  // ([splits, total_q, Hq, D] and [splits, Hq, total_q]); 0 = no split
+  int key_split;
 };
 
 // Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
@@ -211,10 +215,14 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   const int ntok = min(nq - tok0, a.tok_per_tile);
   const int p_first = ctx + tok0;
   const int p_last = p_first + ntok - 1;
-  const int k_hi = a.causal ? min(L, p_last + 1) : L;
-  const int k_lo = a.window_left >= 0 ? max(0, p_first - a.window_left) : 0;
+  int k_hi = a.causal ? min(L, p_last + 1) : L;
+  int k_lo = a.window_left >= 0 ? max(0, p_first - a.window_left) : 0;
+  if (a.key_split > 0) {
+    k_lo = max(k_lo, static_cast<int>(blockIdx.z) * a.key_split);
+    k_hi = min(k_hi, static_cast<int>(blockIdx.z + 1) * a.key_split);
+  }
   const int t_begin = k_lo / kKT;
-  const int t_end = (k_hi + kKT - 1) / kKT;
+  const int t_end = max((k_hi + kKT - 1) / kKT, t_begin);  // empty split: no tile
 
   // this lane's query row
   const int row = wave * 32 + r32;
@@ -247,7 +255,8 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     const int tile = min(t0 + lane, t_end - 1);
     return load4_async(btab + div_magic(group_key(tile), a.bs_magic));
   };
-  uint32_t ids = load_ids(t_begin);
+  uint32_t ids = 0;
+  if (t_end > t_begin) ids = load_ids(t_begin);
 
   // Q fragments (B operand of S^T = K Q^T).  Loaded by asm, like the K/V
   // DMA: a load the compiler tracks would get a wait at its first use that
@@ -547,7 +556,8 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
   const int64_t qrow = q0 + tok0 + tk;
-  uint16_t* orow = a.out + (qrow * a.Hq + head) * D + 4 * g2;
+  const int64_t part = blockIdx.z;  // key split (0 without splits)
+  uint16_t* orow = a.out + ((part * a.total_q + qrow) * a.Hq + head) * D + 4 * g2;
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
@@ -558,12 +568,12 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       *reinterpret_cast<u32x2*>(orow + dc * 32 + 8 * e4) = w;
     }
   if (a.lse != nullptr && g2 == 0)
-    a.lse[(int64_t)head * a.total_q + qrow] =
+    a.lse[(part * a.Hq + head) * a.total_q + qrow] =
         l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
 }
 
 template <typename T, int D, int FEAT>
-int launch_p(const PrefillArgs& args, int max_seqlen_q, hipStream_t stream) {
+int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D, FEAT>),
@@ -575,26 +585,28 @@ int launch_p(const PrefillArgs& args, int max_seqlen_q, hipStream_t stream) {
   a.n_qtiles = (max_seqlen_q + a.tok_per_tile - 1) / a.tok_per_tile;
   if (a.n_qtiles == 0) return 0;
   // (the API bounds Hkv * max_seqlen_q below 2^31 and B by 65535)
-  const dim3 grid(static_cast<unsigned>(a.Hkv * a.n_qtiles), a.B, 1);
+  const int splits = a.key_split > 0 ? n_ksplits : 1;
+  const dim3 grid(static_cast<unsigned>(a.Hkv * a.n_qtiles), a.B, static_cast<unsigned>(splits));
   hipLaunchKernelGGL((prefill_kernel<T, D, FEAT>), grid, dim3(kNW<D> * 64),
                      prefill_lds_bytes<D>(), stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 template <typename T, int D>
-int launch_feat(const PrefillArgs& a, int mq, bool softcap, bool alibi, hipStream_t s) {
-  if (softcap && alibi) return launch_p<T, D, kSoftcap | kAlibi>(a, mq, s);
-  if (softcap) return launch_p<T, D, kSoftcap>(a, mq, s);
-  if (alibi) return launch_p<T, D, kAlibi>(a, mq, s);
-  return launch_p<T, D, 0>(a, mq, s);
+int launch_feat(const PrefillArgs& a, int mq, int ns, bool softcap, bool alibi, hipStream_t s) {
+  if (softcap && alibi) return launch_p<T, D, kSoftcap | kAlibi>(a, mq, ns, s);
+  if (softcap) return launch_p<T, D, kSoftcap>(a, mq, ns, s);
+  if (alibi) return launch_p<T, D, kAlibi>(a, mq, ns, s);
+  return launch_p<T, D, 0>(a, mq, ns, s);
 }
 
 template <typename T>
-int launch_t(const PrefillArgs& a, int D, int mq, bool softcap, bool alibi, hipStream_t s) {
+int launch_t(const PrefillArgs& a, int D, int mq, int ns, bool softcap, bool alibi,
+             hipStream_t s) {
   switch (D) {
-    case 64: return launch_feat<T, 64>(a, mq, softcap, alibi, s);
-    case 128: return launch_feat<T, 128>(a, mq, softcap, alibi, s);
-    default: return launch_feat<T, 256>(a, mq, softcap, alibi, s);
+    case 64: return launch_feat<T, 64>(a, mq, ns, softcap, alibi, s);
+    case 128: return launch_feat<T, 128>(a, mq, ns, softcap, alibi, s);
+    default: return launch_feat<T, 256>(a, mq, ns, softcap, alibi, s);
   }
 }
 
@@ -627,9 +639,12 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.causal = p.causal;
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;
+  a.key_split = p.key_split;
+  const int ns = p.key_split > 0 ? (p.max_seqlen_k + p.key_split - 1) / p.key_split : 1;
   const bool alibi = p.alibi_slopes != nullptr;
-  if (p.dtype == kBF16) return launch_t<BF16>(a, p.head_size, p.max_seqlen_q, softcap, alibi, stream);
-  return launch_t<F16>(a, p.head_size, p.max_seqlen_q, softcap, alibi, stream);
+  if (p.dtype == kBF16)
+    return launch_t<BF16>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+  return launch_t<F16>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
 }
 
 }  // namespace pa

@@ -113,3 +113,27 @@ def test_check_indices_validation(lib):
     assert f(1, 4, 1, 0, 1, 2, 10, 16, 1, None) == -1             # stride
     assert f(1, -1, 1, 8, 1, 2, 10, 16, 1, None) == -1
     assert lib.pa_last_error().startswith("pa_check_indices")
+
+
+def _cascade(pa, **kw):
+    args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
+                num_seqs=2, total_q=5, mq=3, mk=80, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
+                cap=0.0, prefix=32, max_splits=4, parts=1, parts_lse=1, ints=1, dtype=pa.PA_BF16)
+    args.update(kw)
+    return pa.lib.paged_attn_cascade(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(prefix=0), -1), (dict(prefix=24), -1), (dict(prefix=80), -1), (dict(parts=None), -1),
+    (dict(ints=None), -1), (dict(parts_lse=None), -1), (dict(cu=None), -1), (dict(out=None), -1),
+    (dict(d=96), -2), (dict(dtype=2), -2), (dict(bs=20), -1), (dict(cap=-1.0), -1),
+    (dict(max_splits=0), -1), (dict(max_splits=256), -1),
+])
+def test_cascade_validation(lib, kw, code):
+    assert _cascade(lib, **kw) == code
+    assert lib.pa_last_error().startswith("paged_attn_cascade")
+
+
+def test_cascade_empty_is_noop(lib):
+    assert _cascade(lib, num_seqs=0, q=None, kc=None, vc=None, seq_lens=None, bt=None, cu=None,
+                    parts=None, parts_lse=None, ints=None) == 0

@@ -1,0 +1,93 @@
+"""GPU parity of paged_attn_cascade (causal prefill over a shared,
+block-aligned prefix) against the oracle's cascade and plain causal
+attention, in float64: attention outputs to max-abs 2e-2 / mean-abs 2e-3,
+LSE to 1e-2.  The GPU's plain causal prefill of the same batch must agree
+with it to the same bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle_side import assert_attn_close, assert_lse_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_attention_29_amd as pa
+    return pa
+
+
+def _case(seed, prefix, q_lens, extra, Hq, Hkv, D, bs, dtype):
+    """Shared prefix blocks, own blocks after them, random K/V in every block
+    (NaN in the spare blocks), queries after the prefix."""
+    g = torch.Generator().manual_seed(seed)
+    B, n = len(q_lens), prefix // bs
+    lens = [prefix + e + ql for e, ql in zip(extra, q_lens)]
+    own = [-(-(L - prefix) // bs) for L in lens]
+    nb = n + sum(own) + 3
+    perm = torch.randperm(nb, generator=g)
+    table = torch.zeros(B, n + max(own) + 2, dtype=torch.int32)   # 2 spare columns of padding
+    table[:, :n] = perm[:n]
+    at = n
+    for b in range(B):
+        table[b, n:n + own[b]] = perm[at:at + own[b]]
+        at += own[b]
+    kc = torch.randn(nb, bs, Hkv, D, generator=g).to(dtype)
+    vc = torch.randn(nb, bs, Hkv, D, generator=g).to(dtype)
+    for spare in perm[at:].tolist():
+        kc[spare] = float("nan")
+        vc[spare] = float("nan")
+    cu = [0]
+    for ql in q_lens:
+        cu.append(cu[-1] + ql)
+    q = (torch.randn(cu[-1], Hq, D, generator=g) * 0.5).to(dtype)
+    return q, kc, vc, cu, lens, table
+
+
+CASES = [
+    # name, prefix, q_lens, extra context after the prefix, Hq, Hkv, D, bs, dtype, softcap
+    ("g4_d128_bf16", 256, [1, 37, 64, 129, 5, 200], [0, 100, 7, 300, 64, 1], 32, 8, 128, 16,
+     torch.bfloat16, 0.0),
+    ("g2_d64_fp16_cap", 64, [17, 1, 90], [3, 0, 50], 4, 2, 64, 32, torch.float16, 5.0),
+    ("g1_d256", 32, [40, 9], [10, 100], 2, 2, 256, 16, torch.bfloat16, 0.0),
+    # a decode batch: one query per sequence, so the prefix pass splits its keys
+    ("decode_q1_splits", 1024, [1] * 40, list(range(3, 43 * 7, 7)), 32, 8, 128, 16,
+     torch.bfloat16, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_cascade_matches_oracle_and_prefill(pa, case):
+    name, prefix, q_lens, extra, Hq, Hkv, D, bs, dtype, cap = case
+    print(f"\n[gpu-case] cascade {name}", flush=True)
+    q, kc, vc, cu, lens, table = _case(len(name), prefix, q_lens, extra, Hq, Hkv, D, bs, dtype)
+    scale = D ** -0.5
+    dev = dict(device="cuda")
+    qd, kcd, vcd, td = q.cuda(), kc.cuda(), vc.cuda(), table.cuda()
+    cud = torch.tensor(cu, dtype=torch.int32, **dev)
+    lensd = torch.tensor(lens, dtype=torch.int32, **dev)
+    T = cu[-1]
+    out = torch.full((T, Hq, D), float("nan"), dtype=dtype, **dev)
+    lse = torch.full((Hq, T), float("nan"), dtype=torch.float32, **dev)
+    pa.paged_attn_cascade(out, qd, kcd, vcd, cud, lensd, td, max(q_lens), max(lens), scale, prefix,
+                          softcap=cap, lse=lse)
+    out3 = torch.empty_like(out)
+    pa.paged_attn_cascade(out3, qd, kcd, vcd, cud, lensd, td, max(q_lens), max(lens), scale,
+                          prefix, softcap=cap, max_prefix_splits=3)
+    out_p = torch.empty_like(out)
+    lse_p = torch.empty_like(lse)
+    pa.paged_attn_prefill(out_p, qd, kcd, vcd, cud, lensd, td, max(q_lens), max(lens), scale,
+                          True, -1, cap, None, lse=lse_p)
+    torch.cuda.synchronize()
+    ro, rl = oracle.cascade(q, kc, vc, cu, lens, table, scale, prefix, softcap=cap)
+    po, pl = oracle.attend(q, kc, vc, cu, lens, table, scale, True, -1, cap, None)
+    assert torch.allclose(ro, po, atol=1e-10) and torch.allclose(rl, pl, atol=1e-10)
+    assert_attn_close(out, ro, f"{name} cascade")
+    assert_lse_close(lse, rl, f"{name} cascade lse")
+    assert_attn_close(out_p, ro, f"{name} plain prefill")
+    assert_attn_close(out, out_p.double().cpu(), f"{name} cascade vs prefill")
+    assert_attn_close(out3, ro, f"{name} cascade, at most 3 prefix splits")
