@@ -249,12 +249,117 @@ def cpu_baseline(w, seconds: float = 10.0, max_passes: int = 100):
                       f"passes, {elapsed:.1f} s of CPU time, float64"}
 
 
+CASCADE_METRIC = "cascade decode over a shared prefix: effective KV GB/s, bf16 paged KV, 1xMI355X"
+
+
+def run_cascade(args, pa):
+    """A decode step of 64 requests that share a 4096-token prefix (the
+    shape the cascade is for: many requests, a long common prompt), each
+    with its own 64-1024 tokens of history; 32 query / 8 KV heads of 128,
+    block 16, bf16.  Times paged_attn_cascade and, on the same inputs, the
+    plain split decode + merge.  `value` is the plain path's K/V bytes (every
+    key of every sequence) over the cascade's time; the roofline counts the
+    bytes the cascade must read (the prefix once, each suffix once)."""
+    B, P, Hq, Hkv, D, bs, S = 64, 4096, 32, 8, 128, 16, 8
+    rng = np.random.Generator(np.random.PCG64(6))
+    suffix = rng.integers(64, 1024, size=B, endpoint=True)
+    lens = P + suffix
+    n = P // bs
+    own = [-(-int(x) // bs) for x in suffix]
+    nb = n + sum(own)
+    perm = rng.permutation(nb).astype(np.int32)
+    table = np.zeros((B, n + max(own)), np.int32)
+    table[:, :n] = perm[:n]
+    at = n
+    for b in range(B):
+        table[b, n:n + own[b]] = perm[at:at + own[b]]
+        at += own[b]
+    g = torch.Generator(device="cuda").manual_seed(6)
+    # four independent caches used in turn (about 320 MB): more than the
+    # 256 MB Infinity Cache, so no call finds the previous call's K/V there
+    caches = [(torch.randn(nb, bs, Hkv, D, generator=g, device="cuda", dtype=torch.bfloat16),
+               torch.randn(nb, bs, Hkv, D, generator=g, device="cuda", dtype=torch.bfloat16))
+              for _ in range(4)]
+    q = torch.randn(B, Hq, D, generator=g, device="cuda", dtype=torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    seq_lens = torch.from_numpy(lens.astype(np.int32)).cuda()
+    cu = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    scale = D ** -0.5
+    out_c = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    out_d = torch.empty_like(out_c)
+    ws = (torch.empty(17, B, Hq, D, dtype=torch.bfloat16, device="cuda"),
+          torch.empty(17, Hq, B, dtype=torch.float32, device="cuda"),
+          torch.empty(B + 3, dtype=torch.int32, device="cuda"))
+    po = torch.empty(S, B, Hq, D, dtype=torch.float32, device="cuda")
+    pl = torch.empty(S, Hq, B, dtype=torch.float32, device="cuda")
+    mx = int(lens.max())
+
+    turn = [0]
+
+    def next_cache():
+        turn[0] += 1
+        return caches[turn[0] % len(caches)]
+
+    def cascade():
+        kc, vc = next_cache()
+        pa.paged_attn_cascade(out_c, q, kc, vc, cu, seq_lens, bt, 1, mx, scale, P,
+                              max_prefix_splits=16, workspace=ws)
+
+    def plain():
+        kc, vc = next_cache()
+        pa.paged_attn_decode(None, q, kc, vc, seq_lens, bt, mx, scale, num_splits=S,
+                             part_out=po, part_lse=pl)
+        pa.merge_attn_states(out_d, po, pl)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        spin_up(fn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t_c, t_d = timed(cascade), timed(plain)
+    turn[0] = -1
+    cascade()
+    turn[0] = -1
+    plain()  # both on the same cache for the comparison below
+    row = Hkv * D * 2 * 2  # K and V bytes of one key, all KV heads
+    plain_bytes = int(lens.sum()) * row
+    cascade_bytes = (P + int(suffix.sum())) * row
+    diff = (out_c.float() - out_d.float()).abs().max().item()
+    ach = cascade_bytes / (t_c * 1e-3) / 1e9
+    return {
+        "metric": CASCADE_METRIC, "value": round(plain_bytes / (t_c * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_c, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "cascade_decode_b64_prefix4096_suffix64-1024_h32-8-128_bs16",
+                   "num_seqs": B, "common_prefix_len": P, "context_tokens": int(lens.sum()),
+                   "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
+                   "step": "paged_attn_cascade (prefix prefill + suffix prefill + merge)"},
+        "plain_decode": {"ms": round(t_d, 4), "num_splits": S,
+                         "GB/s": round(plain_bytes / (t_d * 1e-3) / 1e9, 1),
+                         "step": "paged_attn_decode + merge_attn_states"},
+        "speedup_vs_plain": round(t_d / t_c, 2),
+        "max_abs_diff_vs_plain": round(diff, 5),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_cascade (whole call)",
+                     "bytes_per_launch": cascade_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "long"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "long", "cascade"])
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
@@ -270,6 +375,9 @@ def main():
     import paged_kv_attention_29_amd as pa
     from paged_kv_attention_29_amd import runner
 
+    if args.workload == "cascade":
+        print(json.dumps(run_cascade(args, pa)), flush=True)
+        return
     if args.workload == "decode":
         w = W.decode_batch() if args.splits is None else W.decode_batch(num_splits=args.splits)
     elif args.workload == "mixed":
