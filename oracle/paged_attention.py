@@ -63,7 +63,7 @@ def gather_sequence(cache: torch.Tensor, block_table_row: torch.Tensor,
 
 
 def _visible(q_pos: torch.Tensor, seq_len: int, causal: bool, window_left: int,
-             key_range: Optional[Sequence[int]]) -> torch.Tensor:
+             key_range: Optional[Sequence[int]], attn_chunk_size: int = 0) -> torch.Tensor:
     """Boolean [n_queries, seq_len]: may query at position p see key j?
 
     * j < seq_len always;
@@ -73,7 +73,12 @@ def _visible(q_pos: torch.Tensor, seq_len: int, causal: bool, window_left: int,
       keys including the query itself (a window w is passed as w - 1)
       [vLLM flash_attn.py (e2f56c3), FlashAttentionImpl.__init__,
       sliding_window -> (sliding_window - 1, 0)];
-    * key_range (lo, hi): lo <= j < hi — the key partition of one split.
+    * key_range (lo, hi): lo <= j < hi — the key partition of one split;
+    * attn_chunk_size > 0 (chunked local attention): j lies in p's chunk,
+      (p // attn_chunk_size) * attn_chunk_size <= j — the positions are cut
+      into chunks of that many tokens and a query sees only its own chunk
+      [vLLM flash_attn.py (v0.9.0.1 docs), make_local_attention_virtual_
+      batches: each query's keys start at its local attention block].
     """
     j = torch.arange(seq_len, dtype=torch.long)[None, :]
     p = q_pos[:, None]
@@ -85,6 +90,8 @@ def _visible(q_pos: torch.Tensor, seq_len: int, causal: bool, window_left: int,
     if key_range is not None:
         lo, hi = key_range
         vis &= (j >= lo) & (j < hi)
+    if attn_chunk_size > 0:
+        vis &= j >= torch.div(p, attn_chunk_size, rounding_mode="floor") * attn_chunk_size
     return vis
 
 
@@ -93,8 +100,11 @@ def attend(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            block_table: torch.Tensor, scale: float, causal: bool = True,
            window_left: int = -1, softcap: float = 0.0,
            alibi_slopes: Optional[torch.Tensor] = None,
-           key_ranges: Optional[Sequence[Sequence[int]]] = None):
+           key_ranges: Optional[Sequence[Sequence[int]]] = None,
+           attn_chunk_size: int = 0):
     """Varlen attention over the paged cache; returns (out, lse) in float64.
+    attn_chunk_size > 0 restricts each query to its own chunk of positions
+    (chunked local attention, see ``_visible``).
 
     q : [total_q, num_heads, head_size]; queries of sequence b are rows
         cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (cu_seqlens_q is the running
@@ -133,7 +143,7 @@ def attend(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         ctx = L - n_q
         q_pos = ctx + torch.arange(n_q, dtype=torch.long)
         vis = _visible(q_pos, L, causal, window_left,
-                       None if key_ranges is None else key_ranges[b])
+                       None if key_ranges is None else key_ranges[b], attn_chunk_size)
         K = gather_sequence(key_cache, block_table[b], L)
         V = gather_sequence(value_cache, block_table[b], L)
         dist = (q_pos[:, None] - torch.arange(L)[None, :]).abs().to(_F64)

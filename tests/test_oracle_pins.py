@@ -462,3 +462,44 @@ def test_cascade_rejects_unshared_prefix():
     table[1, 0] = table[1, 0] + 100
     with pytest.raises(AssertionError):
         oracle.cascade(q, kc, vc, cu, lens, table, 0.5, 32)
+
+
+# ----------------------------------------------------------------------------
+# chunked local attention (next row): keys of the query's own chunk only
+# ----------------------------------------------------------------------------
+def test_chunked_attention_with_one_chunk_is_plain_causal():
+    P = Paged([30, 7], 2, 16, 16, seed=21)
+    q = torch.randn(12, 4, 16)
+    cu = [0, 9, 12]
+    a = oracle.attend(q, P.kc, P.vc, cu, [30, 7], P.table, 0.3, True, attn_chunk_size=32)
+    b = oracle.attend(q, P.kc, P.vc, cu, [30, 7], P.table, 0.3, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_chunked_attention_query_at_chunk_start_sees_itself():
+    P = Paged([40], 1, 8, 16, seed=22)
+    q = torch.randn(9, 2, 8)                    # positions 31..39
+    o, l = oracle.attend(q, P.kc, P.vc, [0, 9], [40], P.table, 0.7, True, attn_chunk_size=8)
+    t = 32 - 31                                 # row of position 32, a chunk start
+    assert torch.equal(o[t], P.V[0][32, 0].double().expand(2, 8))
+    assert torch.allclose(l[:, t], 0.7 * (q[t].double() @ P.K[0][32, 0].double()), atol=1e-14)
+
+
+def test_chunked_attention_equals_causal_attention_per_chunk():
+    """Each chunk of a sequence, taken as its own sequence (its keys from the
+    chunk start), gives the same rows as chunked attention over the whole."""
+    chunk, L, nq = 16, 53, 30                   # queries at positions 23..52
+    P = Paged([L], 2, 8, 16, seed=23)
+    q = torch.randn(nq, 4, 8)
+    o, l = oracle.attend(q, P.kc, P.vc, [0, nq], [L], P.table, 0.4, True, attn_chunk_size=chunk)
+    p0 = L - nq
+    for c0 in range(0, L, chunk):
+        rows = [t for t in range(nq) if c0 <= p0 + t < c0 + chunk]
+        if not rows:
+            continue
+        Lc = p0 + rows[-1] + 1 - c0             # keys c0 .. the chunk's last query
+        table = P.table[:, c0 // 16:]
+        oc, lc = oracle.attend(q[rows[0]:rows[-1] + 1], P.kc, P.vc, [0, len(rows)], [Lc], table,
+                               0.4, True)
+        assert torch.allclose(o[rows[0]:rows[-1] + 1], oc, atol=1e-12, rtol=0)
+        assert torch.allclose(l[:, rows[0]:rows[-1] + 1], lc, atol=1e-12, rtol=0)
