@@ -249,6 +249,64 @@ def cpu_baseline(w, seconds: float = 10.0, max_passes: int = 100):
                       f"passes, {elapsed:.1f} s of CPU time, float64"}
 
 
+LOCAL_METRIC = "chunked local attention prefill (virtual batches): TFLOP/s, bf16 paged KV, 1xMI355X"
+
+
+def run_local(args, pa, runner, chunk: int = 512):
+    """The prefill batch (16 x 256-2048 causal, 32/8/128, block 16) under
+    chunked local attention with attn_chunk_size 512: the host rewriting
+    gives the virtual batch, and the prefill kernel runs over it.  TFLOP/s
+    counts 4 * D * Hq per visible (query, key) pair of the chunked mask."""
+    w = W.prefill_batch()
+    call = w.steps[0].calls[0]
+    cache = runner.PagedCache(w)
+    k, v, s = cache.step_inputs(w.steps[0])
+    pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+    cu = np.concatenate([[0], np.cumsum(call.query_lens)]).astype(np.int32)
+    table = w.block_table[np.asarray(call.seq_ids)]
+    q_loc, cu_loc, k_loc, bt_loc = pa.local_virtual_batches(chunk, cu, call.seq_lens, table,
+                                                            w.block_size)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cu_d, k_d, bt_d = dev(cu_loc), dev(k_loc), dev(bt_loc)
+    q = call.q.cuda()
+    out = torch.empty_like(q)
+    mq, mk = int(q_loc.max()), int(k_loc.max())
+
+    def run():
+        pa.paged_attn_prefill(out, q, cache.key_cache, cache.value_cache, cu_d, k_d, bt_d, mq, mk,
+                              w.scale, True)
+
+    for _ in range(args.warmup):
+        run()
+    spin_up(run)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # causal within each virtual sequence (its queries are its last positions)
+    pairs = sum(nq * (nk - nq) + nq * (nq + 1) // 2 for nq, nk in zip(q_loc.tolist(), k_loc.tolist()))
+    flops = 4 * w.head_size * w.num_heads * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": LOCAL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_local{chunk}", "attn_chunk_size": chunk,
+                   "num_seqs": call.num_seqs, "virtual_seqs": int(q_loc.size),
+                   "query_tokens": int(cu[-1]), "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size},
+        "flops": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_attn_prefill over the virtual batch"},
+    }
+
+
 CASCADE_METRIC = "cascade decode over a shared prefix: effective KV GB/s, bf16 paged KV, 1xMI355X"
 
 
@@ -359,7 +417,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "long", "cascade"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "long", "cascade", "local"])
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
@@ -377,6 +435,9 @@ def main():
 
     if args.workload == "cascade":
         print(json.dumps(run_cascade(args, pa)), flush=True)
+        return
+    if args.workload == "local":
+        print(json.dumps(run_local(args, pa, runner)), flush=True)
         return
     if args.workload == "decode":
         w = W.decode_batch() if args.splits is None else W.decode_batch(num_splits=args.splits)

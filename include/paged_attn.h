@@ -220,6 +220,40 @@ int paged_attn_cascade(void* out, float* lse, const void* q,
                        int32_t* work_ints, pa_dtype_t dtype, void* stream);
 
 /*
+ * pa_local_virtual_batches — HOST-side rewriting of a batch for chunked
+ * local attention [vLLM flash_attn.py (v0.9.0.1 docs),
+ * make_local_attention_virtual_batches]: positions are cut into chunks of
+ * attn_chunk_size tokens and a query sees only the keys of its own chunk up
+ * to itself.  Each (sequence, chunk holding some of its queries) becomes one
+ * virtual sequence whose queries are those rows (same order: q and out stay
+ * as they are), whose keys run from the chunk start to its last query, and
+ * whose block-table row is the sequence's row from the chunk's first block
+ * (attn_chunk_size / block_size entries, clipped to the last column).
+ * paged_attn_prefill (causal) over the virtual batch is the chunked
+ * attention of the original one.
+ *
+ *   All arrays are HOST arrays.  query_start_loc int32 [num_seqs + 1],
+ *   seq_lens int32 [num_seqs] (keys, >= the sequence's queries),
+ *   block_table int32 rows of block_table_stride entries of which the first
+ *   block_table_cols are valid.  attn_chunk_size a positive multiple of
+ *   block_size.
+ *   Outputs (all NULL: only count; else all given, caller-owned, room for
+ *   max_virtual sequences): seqlens_q_local [V], cu_seqlens_q_local [V + 1],
+ *   seqlens_k_local [V], block_table_local [V, attn_chunk_size / block_size].
+ *   Returns V >= 0, the number of virtual sequences, or a negative code
+ *   (nothing written on error).  No device work.
+ */
+int pa_local_virtual_batches(int attn_chunk_size, int block_size,
+                             const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int num_seqs,
+                             const int32_t* block_table,
+                             int64_t block_table_stride, int block_table_cols,
+                             int max_virtual, int32_t* seqlens_q_local,
+                             int32_t* cu_seqlens_q_local,
+                             int32_t* seqlens_k_local,
+                             int32_t* block_table_local);
+
+/*
  * pa_check_indices — debug validation of the device index arrays that the
  * calls above trust (their contents are undefined behaviour when out of
  * range).  Optional, for tests and debugging; not on the hot path.

@@ -30,6 +30,7 @@ __all__ = [
     "paged_attn_decode",
     "merge_attn_states",
     "paged_attn_cascade",
+    "local_virtual_batches",
     "check_indices",
     "pa_last_error",
     "library_path",
@@ -68,8 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_cascade.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _i32,
                                        _i32, _vp, _vp, _vp, _i32, _vp]
+    lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
+                                             _vp, _vp, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states",
-               "pa_check_indices", "paged_attn_cascade"):
+               "pa_check_indices", "paged_attn_cascade", "pa_local_virtual_batches"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -190,6 +193,33 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
         int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), _ptr(ints),
         _code(q.dtype),
         _stream(stream)))
+
+
+def local_virtual_batches(attn_chunk_size: int, query_start_loc, seq_lens, block_table,
+                          block_size: int):
+    """Chunked local attention: the virtual batch for paged_attn_prefill
+    (see pa_local_virtual_batches).  Host numpy int32 arrays in and out:
+    (seqlens_q_local, cu_seqlens_q_local, seqlens_k_local, block_table_local)."""
+    import numpy as np
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    n = lib.pa_local_virtual_batches(int(attn_chunk_size), int(block_size), ptr(qsl), ptr(lens),
+                                     lens.size, None, 0, 0, 0, None, None, None, None)
+    if n < 0:
+        raise PagedAttnError("pa_local_virtual_batches", n, pa_last_error())
+    pages = attn_chunk_size // block_size
+    q_loc = np.zeros(n, np.int32)
+    cu = np.zeros(n + 1, np.int32)
+    k_loc = np.zeros(n, np.int32)
+    bt_loc = np.zeros((n, pages), np.int32)
+    rc = lib.pa_local_virtual_batches(int(attn_chunk_size), int(block_size), ptr(qsl), ptr(lens),
+                                      lens.size, ptr(bt), bt.shape[1], bt.shape[1], n, ptr(q_loc),
+                                      ptr(cu), ptr(k_loc), ptr(bt_loc))
+    if rc < 0:
+        raise PagedAttnError("pa_local_virtual_batches", rc, pa_last_error())
+    return q_loc, cu, k_loc, bt_loc
 
 
 def check_indices(num_blocks: int, block_size: int, slot_mapping: Optional[torch.Tensor] = None,

@@ -316,6 +316,50 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
                     fn);
 }
 
+int pa_local_virtual_batches(int attn_chunk_size, int block_size, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int num_seqs, const int32_t* block_table,
+                             int64_t block_table_stride, int block_table_cols, int max_virtual,
+                             int32_t* seqlens_q_local, int32_t* cu_seqlens_q_local,
+                             int32_t* seqlens_k_local, int32_t* block_table_local) {
+  const char* fn = "pa_local_virtual_batches";
+  if (attn_chunk_size <= 0 || block_size <= 0 || attn_chunk_size % block_size != 0)
+    return fail(PA_ERR_INVALID,
+                "%s: attn_chunk_size (%d) must be a positive multiple of block_size (%d)", fn,
+                attn_chunk_size, block_size);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "%s: num_seqs must be >= 0", fn);
+  if (num_seqs > 0 && (query_start_loc == nullptr || seq_lens == nullptr))
+    return fail(PA_ERR_INVALID, "%s: NULL query_start_loc or seq_lens", fn);
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t q_len = (int64_t)query_start_loc[b + 1] - query_start_loc[b];
+    if (q_len < 0 || seq_lens[b] < q_len)
+      return fail(PA_ERR_INVALID, "%s: sequence %d has %lld queries and %d keys", fn, b,
+                  (long long)q_len, seq_lens[b]);
+  }
+  const bool count_only = seqlens_q_local == nullptr && cu_seqlens_q_local == nullptr &&
+                          seqlens_k_local == nullptr && block_table_local == nullptr;
+  const int v = pa::local_virtual_batches(attn_chunk_size, block_size, query_start_loc, seq_lens,
+                                          num_seqs, nullptr, 0, 0, nullptr, nullptr, nullptr,
+                                          nullptr);
+  if (count_only) {
+    ok();
+    return v;
+  }
+  if (seqlens_q_local == nullptr || cu_seqlens_q_local == nullptr || seqlens_k_local == nullptr ||
+      block_table_local == nullptr)
+    return fail(PA_ERR_INVALID, "%s: outputs must be all NULL (count) or all given", fn);
+  if (v > max_virtual)
+    return fail(PA_ERR_INVALID, "%s: %d virtual sequences exceed max_virtual (%d)", fn, v,
+                max_virtual);
+  if (num_seqs > 0 && (block_table == nullptr || block_table_cols <= 0 ||
+                       block_table_stride < block_table_cols))
+    return fail(PA_ERR_INVALID, "%s: block_table needs cols > 0 and a stride >= cols", fn);
+  pa::local_virtual_batches(attn_chunk_size, block_size, query_start_loc, seq_lens, num_seqs,
+                            block_table, block_table_stride, block_table_cols, seqlens_q_local,
+                            cu_seqlens_q_local, seqlens_k_local, block_table_local);
+  ok();
+  return v;
+}
+
 int pa_check_indices(const int64_t* slot_mapping, int64_t num_tokens, const int32_t* block_table,
                      int64_t block_table_stride, const int32_t* seq_lens, int num_seqs,
                      int64_t num_blocks, int block_size, int32_t* counts, void* stream) {

@@ -50,6 +50,13 @@ struct AttnParams {
 
 int launch_decode(const AttnParams& p, hipStream_t stream);
 
+// host-side rewriting for chunked local attention; returns the number of
+// virtual sequences (outputs NULL: count only)
+int local_virtual_batches(int chunk, int block_size, const int32_t* qsl, const int32_t* seq_lens,
+                          int num_seqs, const int32_t* block_table, int64_t bt_stride,
+                          int bt_cols, int32_t* q_local, int32_t* cu_q_local, int32_t* k_local,
+                          int32_t* bt_local);
+
 int launch_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
                          const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                          int num_seqs, int64_t num_blocks, int block_size, int32_t* counts,
