@@ -101,10 +101,21 @@ def attend(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            window_left: int = -1, softcap: float = 0.0,
            alibi_slopes: Optional[torch.Tensor] = None,
            key_ranges: Optional[Sequence[Sequence[int]]] = None,
-           attn_chunk_size: int = 0):
+           attn_chunk_size: int = 0, sinks: Optional[torch.Tensor] = None):
     """Varlen attention over the paged cache; returns (out, lse) in float64.
     attn_chunk_size > 0 restricts each query to its own chunk of positions
     (chunked local attention, see ``_visible``).
+
+    sinks (attention sinks, one fp32 logit per query head): the pages pass
+    them to the kernels as ``s_aux`` and note that they can be folded into
+    a log-sum-exp [vLLM flash_attn.py (e2f56c3), FlashAttentionImpl.__init__
+    sinks of shape [num_heads]; cascade_attention, s_aux incorporated into
+    the prefix LSE], without printing the formula.  Reading used here: the
+    sink of head h is one more logit in the softmax denominator that carries
+    no value,
+        out = sum_j e^{s_j} V_j / (sum_j e^{s_j} + e^{sink_h}),
+        lse = ln(sum_j e^{s_j} + e^{sink_h}),
+    so a query that sees no key gets out = 0 and lse = sink_h.
 
     q : [total_q, num_heads, head_size]; queries of sequence b are rows
         cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (cu_seqlens_q is the running
@@ -139,7 +150,11 @@ def attend(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
         n_q, L = q1 - q0, int(seq_lens[b])
         if n_q == 0 or L == 0:
-            continue    # no keys: the rows keep out = 0, lse = -inf
+            # no keys: the rows keep out = 0 and lse = -inf (or the sink)
+            if sinks is not None:
+                for h in range(num_heads):
+                    lse[h, q0:q1] = float(sinks[h])
+            continue
         ctx = L - n_q
         q_pos = ctx + torch.arange(n_q, dtype=torch.long)
         vis = _visible(q_pos, L, causal, window_left,
@@ -156,6 +171,17 @@ def attend(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
             if alibi_slopes is not None:
                 s = s - float(alibi_slopes[h]) * dist
             s = torch.where(vis, s, torch.full_like(s, _NEG_INF))
+            if sinks is not None:
+                sk = torch.full((n_q, 1), float(sinks[h]), dtype=_F64)
+                mt = torch.maximum(s.max(dim=1, keepdim=True).values, sk)
+                mt = torch.where(torch.isfinite(mt), mt, torch.zeros_like(mt))
+                w = torch.exp(s - mt)
+                den = w.sum(dim=1, keepdim=True) + torch.exp(sk - mt)
+                o = (w @ V[:, g]) / torch.where(den > 0, den, torch.ones_like(den))
+                out[q0:q1, h] = torch.where(den > 0, o, torch.zeros_like(o))
+                lse[h, q0:q1] = torch.where(den > 0, mt + torch.log(den),
+                                            torch.full_like(den, _NEG_INF))[:, 0]
+                continue
             m = s.max(dim=1, keepdim=True).values
             m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
             w = torch.exp(s - m)                      # exp(-inf) = 0
@@ -171,7 +197,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            seq_lens: Sequence[int], block_table: torch.Tensor, scale: float,
            window_left: int = -1, softcap: float = 0.0,
            alibi_slopes: Optional[torch.Tensor] = None,
-           key_ranges=None):
+           key_ranges=None, sinks: Optional[torch.Tensor] = None):
     """Single-token decode: q [num_seqs, num_heads, head_size], one query per
     sequence at position L_b - 1, which sees every key up to itself.
     [Aphrodite flash_attn.py, FlashAttentionImpl.forward, decode through
@@ -180,7 +206,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
     cu = list(range(B + 1))
     return attend(q, key_cache, value_cache, cu, seq_lens, block_table, scale,
                   causal=True, window_left=window_left, softcap=softcap,
-                  alibi_slopes=alibi_slopes, key_ranges=key_ranges)
+                  alibi_slopes=alibi_slopes, key_ranges=key_ranges, sinks=sinks)
 
 
 def split_bounds(seq_len: int, num_splits: int, block_size: int,
@@ -215,11 +241,13 @@ def split_bounds(seq_len: int, num_splits: int, block_size: int,
 
 def decode_splits(q, key_cache, value_cache, seq_lens, block_table, scale,
                   num_splits: int, window_left: int = -1, softcap: float = 0.0,
-                  alibi_slopes=None, max_seq_len: Optional[int] = None):
+                  alibi_slopes=None, max_seq_len: Optional[int] = None, sinks=None):
     """Partial decode results for each split: parts_out
     [S, num_seqs, num_heads, head_size] and parts_lse [S, num_heads, num_seqs]
     (float64).  An empty split yields out = 0 and lse = -inf.  The splits
-    are sized from max_seq_len (default: the longest sequence)."""
+    are sized from max_seq_len (default: the longest sequence).  Attention
+    sinks, if any, join split 0 only, so the merged result counts each
+    once (as the cascade folds them into its prefix part)."""
     block_size = key_cache.shape[1]
     if max_seq_len is None:
         max_seq_len = max(int(L) for L in seq_lens)
@@ -228,7 +256,8 @@ def decode_splits(q, key_cache, value_cache, seq_lens, block_table, scale,
     for p in range(num_splits):
         o, l = decode(q, key_cache, value_cache, seq_lens, block_table, scale,
                       window_left, softcap, alibi_slopes,
-                      key_ranges=[bounds[b][p] for b in range(len(seq_lens))])
+                      key_ranges=[bounds[b][p] for b in range(len(seq_lens))],
+                      sinks=sinks if p == 0 else None)
         outs.append(o)
         lses.append(l)
     return torch.stack(outs), torch.stack(lses)
@@ -264,7 +293,7 @@ def merge(parts_out: torch.Tensor, parts_lse: torch.Tensor):
 
 def cascade(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
             cu_seqlens_q: Sequence[int], seq_lens: Sequence[int], block_table: torch.Tensor,
-            scale: float, common_prefix_len: int, softcap: float = 0.0):
+            scale: float, common_prefix_len: int, softcap: float = 0.0, sinks=None):
     """Causal varlen attention of a batch whose sequences share their first
     common_prefix_len keys, taken the cascade way [vLLM flash_attn.py
     (e2f56c3), cascade_attention]:
@@ -290,8 +319,10 @@ def cascade(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         q_len = int(cu_seqlens_q[b + 1]) - int(cu_seqlens_q[b])
         assert int(seq_lens[b]) - q_len >= common_prefix_len, "queries must follow the prefix"
         assert torch.equal(block_table[b, :n], block_table[0, :n]), "prefix blocks must be shared"
+    # attention sinks join the prefix part (the page folds s_aux into the
+    # prefix LSE)
     pre_out, pre_lse = attend(q, key_cache, value_cache, [0, total_q], [common_prefix_len],
-                              block_table[:1], scale, causal=False, softcap=softcap)
+                              block_table[:1], scale, causal=False, softcap=softcap, sinks=sinks)
     suf_out, suf_lse = attend(q, key_cache, value_cache, cu_seqlens_q,
                               [int(L) - common_prefix_len for L in seq_lens], block_table[:, n:],
                               scale, causal=True, softcap=softcap)

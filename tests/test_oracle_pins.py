@@ -503,3 +503,66 @@ def test_chunked_attention_equals_causal_attention_per_chunk():
                                0.4, True)
         assert torch.allclose(o[rows[0]:rows[-1] + 1], oc, atol=1e-12, rtol=0)
         assert torch.allclose(l[:, rows[0]:rows[-1] + 1], lc, atol=1e-12, rtol=0)
+
+
+# ----------------------------------------------------------------------------
+# attention sinks (next row): one more logit per head in the denominator
+# ----------------------------------------------------------------------------
+def test_sinks_of_minus_inf_change_nothing():
+    P = Paged([30, 9], 2, 16, 16, seed=31)
+    q = torch.randn(12, 4, 16)
+    cu, lens = [0, 8, 12], [30, 9]
+    a = oracle.attend(q, P.kc, P.vc, cu, lens, P.table, 0.3, True,
+                      sinks=torch.full((4,), float("-inf")))
+    b = oracle.attend(q, P.kc, P.vc, cu, lens, P.table, 0.3, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_sink_with_one_key_is_a_sigmoid_gate():
+    """One visible key with score s and value v: out = v * sigmoid(s - sink),
+    lse = ln(e^s + e^sink)."""
+    P = Paged([1], 1, 8, 16, seed=32)
+    q = torch.randn(1, 2, 8)
+    sinks = torch.tensor([0.7, -1.3])
+    o, l = oracle.decode(q, P.kc, P.vc, [1], P.table, 0.5, sinks=sinks)
+    for h in range(2):
+        s = 0.5 * float(q[0, h].double() @ P.K[0][0, 0].double())
+        gate = 1.0 / (1.0 + math.exp(float(sinks[h]) - s))
+        assert torch.allclose(o[0, h], P.V[0][0, 0].double() * gate, atol=1e-14, rtol=0)
+        assert abs(float(l[h, 0]) - math.log(math.exp(s) + math.exp(float(sinks[h])))) < 1e-13
+
+
+def test_sink_is_an_extra_state_with_zero_output():
+    """Merging the sinkless result with a state (out 0, lse = sink) gives the
+    result with the sink (the LSE merge the pages use for partial states)."""
+    P = Paged([40, 3, 17], 2, 16, 16, seed=33)
+    q = torch.randn(3, 4, 16)
+    sinks = torch.tensor([0.5, -2.0, 3.0, 0.0])
+    o, l = oracle.decode(q, P.kc, P.vc, [40, 3, 17], P.table, 0.25, softcap=2.0, sinks=sinks)
+    o0, l0 = oracle.decode(q, P.kc, P.vc, [40, 3, 17], P.table, 0.25, softcap=2.0)
+    ls = sinks.double()[:, None].expand(4, 3)
+    mo, ml = oracle.merge(torch.stack([o0, torch.zeros_like(o0)]), torch.stack([l0, ls]))
+    assert torch.allclose(o, mo, atol=1e-13, rtol=0) and torch.allclose(l, ml, atol=1e-13, rtol=0)
+
+
+def test_sinks_split_then_merge_and_empty_sequence():
+    P = Paged([0, 60, 33], 2, 8, 16, seed=34)
+    q = torch.randn(3, 4, 8)
+    sinks = torch.tensor([1.0, -0.5, 0.25, 2.0])
+    o, l = oracle.decode(q, P.kc, P.vc, [0, 60, 33], P.table, 0.4, sinks=sinks)
+    po, pl = oracle.decode_splits(q, P.kc, P.vc, [0, 60, 33], P.table, 0.4, 4, sinks=sinks)
+    mo, ml = oracle.merge(po, pl)
+    assert torch.allclose(o, mo, atol=1e-13, rtol=0) and torch.allclose(l, ml, atol=1e-13, rtol=0)
+    assert torch.equal(o[0], torch.zeros(4, 8, dtype=torch.float64))
+    assert torch.equal(l[:, 0], sinks.double())          # no key: the sink alone
+
+
+def test_cascade_with_sinks_equals_plain_causal_with_sinks():
+    """Sinks folded into the prefix part only give the same result as plain
+    causal attention with the sinks."""
+    q, kc, vc, cu, lens, table = _shared_prefix_case(11, 4, 32, [1, 5, 2, 9], [3, 0, 20, 7],
+                                                     8, 2, 16, 16)
+    sinks = torch.tensor([0.3, -1.0, 2.5, 0.0, -0.7, 1.1, 4.0, -3.0])
+    o, l = oracle.cascade(q, kc, vc, cu, lens, table, 0.3, 32, sinks=sinks)
+    ro, rl = oracle.attend(q, kc, vc, cu, lens, table, 0.3, True, sinks=sinks)
+    assert torch.allclose(o, ro, atol=1e-12, rtol=0) and torch.allclose(l, rl, atol=1e-12, rtol=0)
