@@ -99,8 +99,15 @@ int reshape_and_cache(const void* key, const void* value,
  *                   scaled score.
  *   alibi_slopes    nullable; fp32 [num_heads]; adds -slope_h * |p - j|
  *                   after the softcap.
+ *   sinks           nullable; fp32 [num_heads] attention-sink logits [vLLM
+ *                   flash_attn.py (e2f56c3), FlashAttentionImpl sinks,
+ *                   passed to the kernel as s_aux]: each adds e^{sink_h} to
+ *                   its head's softmax denominator and no value, so
+ *                   out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h})
+ *                   and lse = ln(sum_j e^{s_j} + e^{sink_h}).
  *   Query head h reads KV head h / (num_heads / num_kv_heads).
- *   A query that sees no key gets out = 0 and lse = -inf.
+ *   A query that sees no key gets out = 0 and lse = -inf (lse = sink_h
+ *   with sinks).
  *   PA_ERR_UNSUPPORTED also for num_seqs > 65535, more than 128 query heads
  *   per KV head, max_seqlen_k >= 2^24 or num_kv_heads * max_seqlen_q >=
  *   2^31 (grid limits).
@@ -113,8 +120,8 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
                        int max_seqlen_k, int num_heads, int num_kv_heads,
                        int head_size, int block_size, int64_t num_blocks,
                        float scale, int causal, int window_left, float softcap,
-                       const float* alibi_slopes, pa_dtype_t dtype,
-                       void* stream);
+                       const float* alibi_slopes, const float* sinks,
+                       pa_dtype_t dtype, void* stream);
 
 /*
  * paged_attn_decode — one query token per sequence over the paged cache,
@@ -143,7 +150,9 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
  *                   merge_attn_states(out, lse, part_out, part_lse,
  *                   num_splits, num_seqs, num_heads, head_size, PA_F32, ...).
  *   max_seq_len     host upper bound of seq_lens (sizes the splits).
- *   window_left, softcap, alibi_slopes as for prefill.  num_splits <= 256.
+ *   window_left, softcap, alibi_slopes, sinks as for prefill.  With
+ *   num_splits > 1 the sinks join split 0 only, so the merged result
+ *   counts each once.  num_splits <= 256.
  *   num_heads / num_kv_heads must be at most 16.
  */
 int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
@@ -153,8 +162,9 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
                       int num_seqs, int max_seq_len, int num_heads,
                       int num_kv_heads, int head_size, int block_size,
                       int64_t num_blocks, float scale, int window_left,
-                      float softcap, const float* alibi_slopes, int num_splits,
-                      pa_dtype_t dtype, void* stream);
+                      float softcap, const float* alibi_slopes,
+                      const float* sinks, int num_splits, pa_dtype_t dtype,
+                      void* stream);
 
 /*
  * merge_attn_states — combine partial attention results by their
@@ -189,6 +199,8 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
  *
  *   Arguments as for paged_attn_prefill (causal, no window, no ALiBi: the
  *   page's cascade supports neither), plus
+ *   sinks              nullable, as for prefill; folded into the prefix
+ *                      part only (the page adds s_aux to the prefix LSE);
  *   common_prefix_len  > 0, a multiple of block_size, below max_seqlen_k.
  *                      The caller guarantees (device data, not checked):
  *                      the first common_prefix_len / block_size entries of
@@ -215,8 +227,9 @@ int paged_attn_cascade(void* out, float* lse, const void* q,
                        int num_seqs, int64_t total_q, int max_seqlen_q,
                        int max_seqlen_k, int num_heads, int num_kv_heads,
                        int head_size, int block_size, int64_t num_blocks,
-                       float scale, float softcap, int common_prefix_len,
-                       int max_prefix_splits, void* parts_out, float* parts_lse,
+                       float scale, float softcap, const float* sinks,
+                       int common_prefix_len, int max_prefix_splits,
+                       void* parts_out, float* parts_lse,
                        int32_t* work_ints, pa_dtype_t dtype, void* stream);
 
 /*

@@ -60,15 +60,15 @@ def _load() -> ctypes.CDLL:
                                       _i32, _i32, _vp]
     lib.paged_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32,
-                                       _f32, _vp, _i32, _vp]
+                                       _f32, _vp, _vp, _i32, _vp]
     lib.paged_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
-                                      _i32, _i32, _vp]
+                                      _vp, _i32, _i32, _vp]
     lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
     lib.pa_check_indices.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i32, _vp, _vp]
     lib.paged_attn_cascade.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
-                                       _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _i32,
-                                       _i32, _vp, _vp, _vp, _i32, _vp]
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _vp,
+                                       _i32, _i32, _vp, _vp, _vp, _i32, _vp]
     lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
                                              _vp, _vp, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states",
@@ -129,14 +129,16 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        max_seqlen_k: int, scale: float, causal: bool = True,
                        window_left: int = -1, softcap: float = 0.0,
                        alibi_slopes: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                       lse: Optional[torch.Tensor] = None, stream=None,
+                       sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     total_q, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     _check("paged_attn_prefill", lib.paged_attn_prefill(
         _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), seq_lens.numel(), total_q,
         int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
-        int(window_left), float(softcap), _ptr(alibi_slopes), _code(q.dtype), _stream(stream)))
+        int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks), _code(q.dtype),
+        _stream(stream)))
     return out
 
 
@@ -147,14 +149,15 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
                       alibi_slopes: Optional[torch.Tensor] = None, num_splits: int = 1,
                       part_out: Optional[torch.Tensor] = None,
                       part_lse: Optional[torch.Tensor] = None,
-                      lse: Optional[torch.Tensor] = None, stream=None) -> None:
+                      lse: Optional[torch.Tensor] = None, stream=None,
+                      sinks: Optional[torch.Tensor] = None) -> None:
     b, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse), _ptr(q), _ptr(key_cache),
         _ptr(value_cache), _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b,
         int(max_seq_len), hq, hkv, d, bs, nb, float(scale), int(window_left), float(softcap),
-        _ptr(alibi_slopes), int(num_splits), _code(q.dtype), _stream(stream)))
+        _ptr(alibi_slopes), _ptr(sinks), int(num_splits), _code(q.dtype), _stream(stream)))
 
 
 def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: torch.Tensor,
@@ -172,7 +175,8 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        seq_lens: torch.Tensor, block_table: torch.Tensor, max_seqlen_q: int,
                        max_seqlen_k: int, scale: float, common_prefix_len: int,
                        softcap: float = 0.0, lse: Optional[torch.Tensor] = None,
-                       max_prefix_splits: int = 16, workspace=None, stream=None) -> None:
+                       max_prefix_splits: int = 16, workspace=None, stream=None,
+                       sinks: Optional[torch.Tensor] = None) -> None:
     """Causal prefill over a shared prefix (see paged_attn_cascade in the
     header).  ``workspace`` is (parts_out, parts_lse, work_ints) sized for
     max_prefix_splits + 1 parts; it is allocated here with torch when not
@@ -189,7 +193,7 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
     _check("paged_attn_cascade", lib.paged_attn_cascade(
         _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b, t, int(max_seqlen_q),
-        int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), float(softcap),
+        int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), float(softcap), _ptr(sinks),
         int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), _ptr(ints),
         _code(q.dtype),
         _stream(stream)))

@@ -122,7 +122,7 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
                        int max_seqlen_q, int max_seqlen_k, int num_heads, int num_kv_heads,
                        int head_size, int block_size, int64_t num_blocks, float scale, int causal,
                        int window_left, float softcap, const float* alibi_slopes,
-                       pa_dtype_t dtype, void* stream) {
+                       const float* sinks, pa_dtype_t dtype, void* stream) {
   const char* fn = "paged_attn_prefill";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, window_left, softcap, dtype, q, key_cache,
@@ -165,6 +165,7 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
   p.window_left = window_left;
   p.softcap = softcap;
   p.alibi_slopes = alibi_slopes;
+  p.sinks = sinks;
   p.num_splits = 1;
   p.dtype = static_cast<pa::Dtype>(dtype);
   return hip_result(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), fn);
@@ -175,8 +176,8 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
                       const int32_t* block_table, int64_t block_table_stride, int num_seqs,
                       int max_seq_len, int num_heads, int num_kv_heads, int head_size,
                       int block_size, int64_t num_blocks, float scale, int window_left,
-                      float softcap, const float* alibi_slopes, int num_splits,
-                      pa_dtype_t dtype, void* stream) {
+                      float softcap, const float* alibi_slopes, const float* sinks,
+                      int num_splits, pa_dtype_t dtype, void* stream) {
   const char* fn = "paged_attn_decode";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, window_left, softcap, dtype, q, key_cache,
@@ -218,6 +219,7 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
   p.window_left = window_left;
   p.softcap = softcap;
   p.alibi_slopes = alibi_slopes;
+  p.sinks = sinks;
   p.num_splits = num_splits;
   p.dtype = static_cast<pa::Dtype>(dtype);
   return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
@@ -252,7 +254,8 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
                        int64_t block_table_stride, int num_seqs, int64_t total_q,
                        int max_seqlen_q, int max_seqlen_k, int num_heads, int num_kv_heads,
                        int head_size, int block_size, int64_t num_blocks, float scale,
-                       float softcap, int common_prefix_len, int max_prefix_splits,
+                       float softcap, const float* sinks, int common_prefix_len,
+                       int max_prefix_splits,
                        void* parts_out, float* parts_lse, int32_t* work_ints, pa_dtype_t dtype,
                        void* stream) {
   const char* fn = "paged_attn_cascade";
@@ -309,6 +312,7 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
   p.window_left = -1;
   p.softcap = softcap;
   p.alibi_slopes = nullptr;
+  p.sinks = sinks;
   p.num_splits = 1;
   p.dtype = static_cast<pa::Dtype>(dtype);
   return hip_result(pa::launch_cascade(p, common_prefix_len, max_prefix_splits, parts_out,

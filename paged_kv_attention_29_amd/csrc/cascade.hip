@@ -68,7 +68,7 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
   pre.max_seqlen_q = static_cast<int>(T);
   pre.max_seqlen_k = prefix;
   pre.causal = 0;
-  pre.key_split = splits > 1 ? key_split : 0;
+  pre.key_split = splits > 1 ? key_split : 0;  // sinks (if any) join split 0
   int rc = launch_prefill(pre, stream);
   if (rc != 0) return rc;
 
@@ -82,6 +82,7 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
   suf.max_seqlen_k = p.max_seqlen_k - prefix;
   suf.causal = 1;
   suf.key_split = 0;
+  suf.sinks = nullptr;  // counted once, in the prefix part
   rc = launch_prefill(suf, stream);
   if (rc != 0) return rc;
 

@@ -52,6 +52,9 @@ struct DecodeArgs {
   float cap_log2;       // softcap * log2(e)
   int window_left;      // -1 = none
   const float* alibi;   // nullable
+  // attention sinks [Hq] (fp32, nullable): one more logit per head in the
+  // softmax denominator, without a value; folded into split 0 only
+  const float* sinks;
 };
 
 enum { kSoftcap = 1, kAlibi = 2 };
@@ -332,12 +335,19 @@ struct Dec {
       if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.B + b] = lse;
     }
   }
-  // An item without visible keys: zero output, -inf log-sum-exp.
+  // Sink logit of column j in log2 units, or -inf (no sinks, or a split
+  // other than 0).
+  static __device__ __forceinline__ float sink_of(const DecodeArgs& a, int g0, int split, int j) {
+    return a.sinks != nullptr && split == 0 ? a.sinks[g0 * a.G + j] * kLog2e : kNegInf;
+  }
+  // An item without visible keys: zero output, log-sum-exp -inf (or the
+  // sink in split 0).
   static __device__ __forceinline__ void emit_empty(const DecodeArgs& a, int g0, int b,
                                                     int split) {
     for (int idx = threadIdx.x; idx < a.G * HPW * (D / 4); idx += kWaves * 64) {
       const int j = idx / (D / 4);
-      emit4(a, g0, b, split, j, (idx - j * (D / 4)) * 4, v4f{0.f, 0.f, 0.f, 0.f}, kNegInf);
+      emit4(a, g0, b, split, j, (idx - j * (D / 4)) * 4, v4f{0.f, 0.f, 0.f, 0.f},
+            sink_of(a, g0, split, j) * kLn2);
     }
   }
 
@@ -365,7 +375,8 @@ struct Dec {
       const int j = idx / (D / 4);
       const int d = (idx - j * (D / 4)) * 4;
       f2 ml[kWaves];
-      float M = kNegInf;
+      const float sk = sink_of(a, it.g0, it.split, j);  // (max sk, sum 1, output 0)
+      float M = sk;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         ml[w] = *reinterpret_cast<const f2*>(comb + (w * GC + j) * CP);
@@ -374,6 +385,7 @@ struct Dec {
       v4f num = {0.f, 0.f, 0.f, 0.f};
       float den = 0.f;
       if (M != kNegInf) {
+        den = fast_exp2(sk - M);  // 0 without a sink
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float fw = fast_exp2(ml[w][0] - M);
@@ -527,6 +539,7 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.cap_log2 = p.softcap * kLog2e;
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;
+  a.sinks = p.sinks;
   const bool alibi = p.alibi_slopes != nullptr;
   if (p.dtype == kBF16) return launch_t<BF16>(a, p.head_size, softcap, alibi, stream);
   return launch_t<F16>(a, p.head_size, softcap, alibi, stream);

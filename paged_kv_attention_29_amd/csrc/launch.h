@@ -43,6 +43,7 @@ struct AttnParams {
   int window_left;
   float softcap;
   const float* alibi_slopes;
+  const float* sinks;  // [Hq] fp32 attention-sink logits or null; split 0 only
   int num_splits;
   int key_split;  // prefill only: keys per split (a multiple of 64), 0 = none
   Dtype dtype;

@@ -73,6 +73,9 @@ struct PrefillArgs {
   // and writes its normalised partial result and LSE as part z of out / lse
   // ([splits, total_q, Hq, D] and [splits, Hq, total_q]); 0 = no split
   int key_split;
+  // attention sinks [Hq] (fp32, nullable): one more logit per head in the
+  // softmax denominator, without a value; folded into split 0 only
+  const float* sinks;
 };
 
 // Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
@@ -552,9 +555,20 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   }
 
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
-  const float l_tot = l_run + shfl_xor(l_run, 32);
+  float l_tot = l_run + shfl_xor(l_run, 32);
   if (!row_ok) return;
-  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
+  float m_fin = m_run, o_scale = 1.0f;
+  if (a.sinks != nullptr && blockIdx.z == 0) {
+    // the sink as one more state (max sk, sum 1, output 0)
+    const float sk = a.sinks[head] * kLog2e;
+    const float M = fmaxf(m_run, sk);
+    if (M != kNegInf) {
+      o_scale = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
+      l_tot = l_tot * o_scale + fast_exp2(sk - M);
+      m_fin = M;
+    }
+  }
+  const float inv = l_tot > 0.f ? o_scale * __builtin_amdgcn_rcpf(l_tot) : 0.0f;
   const int64_t qrow = q0 + tok0 + tk;
   const int64_t part = blockIdx.z;  // key split (0 without splits)
   uint16_t* orow = a.out + ((part * a.total_q + qrow) * a.Hq + head) * D + 4 * g2;
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     }
   if (a.lse != nullptr && g2 == 0)
     a.lse[(part * a.Hq + head) * a.total_q + qrow] =
-        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+        l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : kNegInf;
 }
 
 template <typename T, int D, int FEAT>
@@ -640,6 +654,7 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;
   a.key_split = p.key_split;
+  a.sinks = p.sinks;
   const int ns = p.key_split > 0 ? (p.max_seqlen_k + p.key_split - 1) / p.key_split : 1;
   const bool alibi = p.alibi_slopes != nullptr;
   if (p.dtype == kBF16)

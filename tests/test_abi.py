@@ -42,7 +42,7 @@ def lib():
 def _decode(pa, **kw):
     args = dict(out=1, lse=None, part_out=None, part_lse=None, q=1, kc=1, vc=1, seq_lens=1,
                 bt=1, bt_stride=4, num_seqs=2, max_seq_len=10, hq=4, hkv=2, d=64, bs=16, nb=8,
-                scale=0.125, wl=-1, cap=0.0, alibi=None, splits=1, dtype=pa.PA_F16)
+                scale=0.125, wl=-1, cap=0.0, alibi=None, sinks=None, splits=1, dtype=pa.PA_F16)
     args.update(kw)
     return pa.lib.paged_attn_decode(*args.values(), None)
 
@@ -50,7 +50,7 @@ def _decode(pa, **kw):
 def _prefill(pa, **kw):
     args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
                 num_seqs=1, total_q=5, mq=5, mk=23, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
-                causal=1, wl=-1, cap=0.0, alibi=None, dtype=pa.PA_F16)
+                causal=1, wl=-1, cap=0.0, alibi=None, sinks=None, dtype=pa.PA_F16)
     args.update(kw)
     return pa.lib.paged_attn_prefill(*args.values(), None)
 
@@ -118,7 +118,7 @@ def test_check_indices_validation(lib):
 def _cascade(pa, **kw):
     args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
                 num_seqs=2, total_q=5, mq=3, mk=80, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
-                cap=0.0, prefix=32, max_splits=4, parts=1, parts_lse=1, ints=1, dtype=pa.PA_BF16)
+                cap=0.0, sinks=None, prefix=32, max_splits=4, parts=1, parts_lse=1, ints=1, dtype=pa.PA_BF16)
     args.update(kw)
     return pa.lib.paged_attn_cascade(*args.values(), None)
 
