@@ -115,6 +115,8 @@ def run_decode(args, pa, runner, w):
         c.key_cache = base.key_cache.clone()
         c.value_cache = base.value_cache.clone()
         caches.append(c)
+    for c in caches:
+        c.sinks = bench_sinks(args, w)
     k, v, s = base.step_inputs(w.steps[0])
     bufs = [c.call_buffers(call, args.splits) for c in caches]
     torch.cuda.synchronize()
@@ -140,13 +142,13 @@ def run_decode(args, pa, runner, w):
             with dec_t:
                 pa.paged_attn_decode(None, cb.q, c.key_cache, c.value_cache, cb.seq_lens,
                                      cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
-                                     w.softcap, c.alibi, cb.num_splits, **kw)
+                                     w.softcap, c.alibi, cb.num_splits, sinks=c.sinks, **kw)
             with merge_t:
                 pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
         else:
             pa.paged_attn_decode(None, cb.q, c.key_cache, c.value_cache, cb.seq_lens,
                                  cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
-                                 w.softcap, c.alibi, cb.num_splits, **kw)
+                                 w.softcap, c.alibi, cb.num_splits, sinks=c.sinks, **kw)
             pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
 
     for i in range(args.warmup):
@@ -168,6 +170,14 @@ def run_decode(args, pa, runner, w):
                 tokens=int(s.numel()))
 
 
+def bench_sinks(args, w):
+    """--sinks: seeded fp32 attention-sink logits, one per query head."""
+    if not args.sinks:
+        return None
+    g = torch.Generator().manual_seed(77)
+    return (torch.randn(w.num_heads, generator=g) * 2.0).to("cuda")
+
+
 def spin_up(fn, seconds: float = WARM_SECONDS):
     """More untimed warm-up: repeat fn until `seconds` of GPU work have run,
     so the timed region sees steady-state clocks."""
@@ -183,6 +193,7 @@ def run_prefill(args, pa, runner):
     w = W.prefill_batch()
     call = w.steps[0].calls[0]
     cache = runner.PagedCache(w)
+    cache.sinks = bench_sinks(args, w)
     k, v, s = cache.step_inputs(w.steps[0])
     cb = cache.call_buffers(call)
     pre_t, rac_t = Timed(), Timed()
@@ -213,7 +224,7 @@ def run_prefill(args, pa, runner):
     }
 
 
-def cpu_baseline(w, seconds: float = 10.0, max_passes: int = 100):
+def cpu_baseline(w, seconds: float = 10.0, max_passes: int = 100, sinks=None):
     """The oracle (float64 PyTorch on the host) on the same decode batch:
     every sequence's K/V is placed in a cache of its own once, then whole
     passes over the batch are timed until about `seconds` of work."""
@@ -239,7 +250,7 @@ def cpu_baseline(w, seconds: float = 10.0, max_passes: int = 100):
         for b, L, kc, vc, table, nbytes in setups:
             t0 = time.perf_counter()
             oracle.decode(call.q[b:b + 1], kc, vc, [L], table, w.scale, w.window_left,
-                          w.softcap, w.alibi_slopes)
+                          w.softcap, w.alibi_slopes, sinks=sinks)
             elapsed += time.perf_counter() - t0
             done_bytes += nbytes
         passes += 1
@@ -422,6 +433,8 @@ def main():
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sinks", action="store_true",
+                    help="decode/mixed/long: pass per-head attention-sink logits")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -471,7 +484,8 @@ def main():
                    "context_tokens": int(call.seq_lens.sum()), "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
                    "block_size": w.block_size, "num_splits": args.splits,
-                   "layers": args.layers, "step": "reshape_and_cache + decode + merge"},
+                   "layers": args.layers, "step": "reshape_and_cache + decode + merge",
+                   "attention_sinks": bool(args.sinks)},
         "kernels_ms": {"reshape_and_cache": round(r["rac_ms"], 4),
                        "paged_attn_decode": round(r["decode_ms"], 4),
                        "merge_attn_states": round(r["merge_ms"], 4)},
@@ -483,7 +497,8 @@ def main():
     if not args.no_prefill and args.workload == "decode":
         out["prefill"] = run_prefill(args, pa, runner)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        sk = bench_sinks(args, w)
+        out["cpu_baseline"] = cpu_baseline(w, sinks=None if sk is None else sk.cpu())
     print(json.dumps(out), flush=True)
 
 

@@ -45,6 +45,7 @@ class PagedCache:
         self.value_cache = torch.full(shape, float("nan"), dtype=w.dtype, device=device)
         self.block_table = torch.from_numpy(w.block_table).to(device)
         self.alibi = None if w.alibi_slopes is None else w.alibi_slopes.to(device)
+        self.sinks = None  # optional fp32 [num_heads] attention-sink logits on the device
 
     def write(self, key: torch.Tensor, value: torch.Tensor, slots: torch.Tensor) -> None:
         reshape_and_cache(key.to(self.device), value.to(self.device), self.key_cache,
@@ -85,16 +86,16 @@ class PagedCache:
             paged_attn_prefill(cb.out, cb.q, self.key_cache, self.value_cache, cb.cu_seqlens_q,
                                cb.seq_lens, cb.block_table, cb.max_seqlen_q, cb.max_seqlen_k,
                                w.scale, True, w.window_left, w.softcap, self.alibi, lse=cb.lse,
-                               stream=stream)
+                               stream=stream, sinks=self.sinks)
         elif cb.num_splits == 1:
             paged_attn_decode(cb.out, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
-                              self.alibi, 1, lse=cb.lse, stream=stream)
+                              self.alibi, 1, lse=cb.lse, stream=stream, sinks=self.sinks)
         else:
             paged_attn_decode(None, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
                               self.alibi, cb.num_splits, part_out=cb.part_out,
-                              part_lse=cb.part_lse, stream=stream)
+                              part_lse=cb.part_lse, stream=stream, sinks=self.sinks)
             merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse, stream=stream)
 
 
