@@ -18,6 +18,10 @@ mathematics independent of this code:
 * ``merge``          — closed forms (identical states, -inf parts).
 * ``cascade``        — equals plain causal ``attend`` (itself pinned above)
                         on batches that share a block-aligned prefix.
+* ``fp8``            — e4m3 code table and quantiser against torch's
+                        float8_e4m3fn type, closed-form codes, the rounding
+                        error bound.  An fp8 cache is attended by passing
+                        its dequantised float64 copy to ``attend``.
 
 Readings the pages leave open (softcap/ALiBi order, ALiBi slope index,
 window edge) are fixed by the readings documented with each function; they
@@ -34,6 +38,7 @@ from .paged_attention import (
     merge,
     cascade,
 )
+from . import fp8
 
 __all__ = [
     "scatter",
@@ -44,4 +49,5 @@ __all__ = [
     "decode_splits",
     "merge",
     "cascade",
+    "fp8",
 ]
