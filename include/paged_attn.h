@@ -24,8 +24,19 @@
  *  - Contents of device arrays (slot ids, block ids, lengths) are trusted:
  *    an out-of-range block id or slot is undefined behaviour
  *    (pa_check_indices counts such entries, for tests and debugging).
- *  - dtype of q / key / value / caches / out: PA_F16 or PA_BF16.  All
- *    arithmetic is fp32; outputs are rounded to nearest-even.
+ *  - dtype of q / key / value / out: PA_F16 or PA_BF16.  All arithmetic is
+ *    fp32; outputs are rounded to nearest-even.
+ *  - kv_cache_dtype: the caches' element type, either dtype itself or
+ *    PA_FP8_E4M3 [vLLM flash_attn.py (e2f56c3), get_fp8_dtype_for_flashattn:
+ *    "fp8" / "fp8_e4m3" is float8_e4m3fn; FlashAttentionImpl.forward, the
+ *    kv_cache_dtype, k_scale and v_scale of reshape_and_cache_flash and the
+ *    k/v descales of the attention call].  An fp8 cache holds one-byte OCP
+ *    e4m3 codes (same shape, 1 byte per element) and takes two device fp32
+ *    scalars k_scale / v_scale: the code of an element x is x / scale
+ *    (fp32, correctly rounded) rounded to the nearest e4m3 value, ties to
+ *    even, saturating at +-448 (NaN stays NaN); the attention reads
+ *    value(code) * scale.  The query stays in dtype.  With a 16-bit cache
+ *    k_scale / v_scale are ignored (may be NULL).
  *  - head_size must be 64, 128 or 256; block_size a positive multiple of 16
  *    and at most 256; num_heads a multiple of num_kv_heads.
  */
@@ -38,7 +49,7 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F32 = 2 } pa_dtype_t;
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F32 = 2, PA_FP8_E4M3 = 3 } pa_dtype_t;
 
 enum {
   PA_OK = 0,
@@ -62,8 +73,12 @@ enum {
  *                   slot / block_size, offset slot % block_size.  A negative
  *                   slot is padding and is skipped.  num_tokens is the length
  *                   of slot_mapping; key/value may hold more (padded) rows.
- *   Copies are bit-exact (kv_cache_dtype "auto": no conversion).  Two tokens
- *   mapped to the same slot race (the caller must not do that).
+ *   dtype           of key / value (PA_F16 or PA_BF16).
+ *   kv_cache_dtype  dtype: rows are copied bit-exactly (kv_cache_dtype
+ *                   "auto", no conversion); PA_FP8_E4M3: each element is
+ *                   quantised with k_scale (keys) or v_scale (values) as
+ *                   described above, and the caches hold the codes.
+ *   Two tokens mapped to the same slot race (the caller must not do that).
  *   num_tokens == 0 is a no-op.
  */
 int reshape_and_cache(const void* key, const void* value,
@@ -71,7 +86,9 @@ int reshape_and_cache(const void* key, const void* value,
                       void* key_cache, void* value_cache,
                       const int64_t* slot_mapping, int64_t num_tokens,
                       int64_t num_blocks, int block_size, int num_kv_heads,
-                      int head_size, pa_dtype_t dtype, void* stream);
+                      int head_size, pa_dtype_t dtype,
+                      pa_dtype_t kv_cache_dtype, const float* k_scale,
+                      const float* v_scale, void* stream);
 
 /*
  * paged_attn_prefill — variable-length attention of new query tokens over
@@ -108,6 +125,8 @@ int reshape_and_cache(const void* key, const void* value,
  *   Query head h reads KV head h / (num_heads / num_kv_heads).
  *   A query that sees no key gets out = 0 and lse = -inf (lse = sink_h
  *   with sinks).
+ *   kv_cache_dtype  must equal dtype here: an fp8 cache gives
+ *                   PA_ERR_UNSUPPORTED (it is read by paged_attn_decode).
  *   PA_ERR_UNSUPPORTED also for num_seqs > 65535, more than 128 query heads
  *   per KV head, max_seqlen_k >= 2^24 or num_kv_heads * max_seqlen_q >=
  *   2^31 (grid limits).
@@ -121,7 +140,9 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
                        int head_size, int block_size, int64_t num_blocks,
                        float scale, int causal, int window_left, float softcap,
                        const float* alibi_slopes, const float* sinks,
-                       pa_dtype_t dtype, void* stream);
+                       pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
+                       const float* k_scale, const float* v_scale,
+                       void* stream);
 
 /*
  * paged_attn_decode — one query token per sequence over the paged cache,
@@ -153,6 +174,9 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
  *   window_left, softcap, alibi_slopes, sinks as for prefill.  With
  *   num_splits > 1 the sinks join split 0 only, so the merged result
  *   counts each once.  num_splits <= 256.
+ *   kv_cache_dtype, k_scale, v_scale: a 16-bit cache (= dtype) or an fp8
+ *   cache with its scales (see the conventions above); the K scale
+ *   multiplies every score and the V scale the result.
  *   num_heads / num_kv_heads must be at most 16.
  */
 int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
@@ -164,7 +188,8 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
                       int64_t num_blocks, float scale, int window_left,
                       float softcap, const float* alibi_slopes,
                       const float* sinks, int num_splits, pa_dtype_t dtype,
-                      void* stream);
+                      pa_dtype_t kv_cache_dtype, const float* k_scale,
+                      const float* v_scale, void* stream);
 
 /*
  * merge_attn_states — combine partial attention results by their
@@ -197,8 +222,8 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
  * with causal = 1 on the same batch; the shared prefix is read once for the
  * batch rather than once per sequence.
  *
- *   Arguments as for paged_attn_prefill (causal, no window, no ALiBi: the
- *   page's cascade supports neither), plus
+ *   Arguments as for paged_attn_prefill (16-bit cache only; causal, no
+ *   window, no ALiBi: the page's cascade supports neither), plus
  *   sinks              nullable, as for prefill; folded into the prefix
  *                      part only (the page adds s_aux to the prefix LSE);
  *   common_prefix_len  > 0, a multiple of block_size, below max_seqlen_k.
@@ -230,7 +255,9 @@ int paged_attn_cascade(void* out, float* lse, const void* q,
                        float scale, float softcap, const float* sinks,
                        int common_prefix_len, int max_prefix_splits,
                        void* parts_out, float* parts_lse,
-                       int32_t* work_ints, pa_dtype_t dtype, void* stream);
+                       int32_t* work_ints, pa_dtype_t dtype,
+                       pa_dtype_t kv_cache_dtype, const float* k_scale,
+                       const float* v_scale, void* stream);
 
 /*
  * pa_local_virtual_batches — HOST-side rewriting of a batch for chunked

@@ -39,7 +39,7 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpagedattn.so")
 
-PA_F16, PA_BF16, PA_F32 = 0, 1, 2
+PA_F16, PA_BF16, PA_F32, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
 
 _vp, _i64, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -57,18 +57,18 @@ def _load() -> ctypes.CDLL:
             f"{library_path} is missing: build it with `python paged_kv_attention_29_amd/build.py`")
     lib = ctypes.CDLL(library_path)
     lib.reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
-                                      _i32, _i32, _vp]
+                                      _i32, _i32, _i32, _vp, _vp, _vp]
     lib.paged_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32,
-                                       _f32, _vp, _vp, _i32, _vp]
+                                       _f32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
     lib.paged_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
-                                      _vp, _i32, _i32, _vp]
+                                      _vp, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
     lib.pa_check_indices.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i32, _vp, _vp]
     lib.paged_attn_cascade.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _vp,
-                                       _i32, _i32, _vp, _vp, _vp, _i32, _vp]
+                                       _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
     lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
                                              _vp, _vp, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states",
@@ -98,6 +98,8 @@ def _code(t: torch.dtype) -> int:
         return PA_BF16
     if t == torch.float32:
         return PA_F32
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3   # an fp8 cache (e4m3 codes)
     raise TypeError(f"unsupported dtype {t}")
 
 
@@ -114,13 +116,17 @@ def _stream(stream) -> Optional[int]:
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
-                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
-    """Write key/value rows [i] into slot slot_mapping[i]; negative slots skip."""
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None,
+                      k_scale: Optional[torch.Tensor] = None,
+                      v_scale: Optional[torch.Tensor] = None) -> None:
+    """Write key/value rows [i] into slot slot_mapping[i]; negative slots skip.
+    A uint8 / float8_e4m3fn cache is quantised with the device fp32 scalars
+    k_scale / v_scale."""
     nb, bs, hkv, d = key_cache.shape
     _check("reshape_and_cache", lib.reshape_and_cache(
         _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_cache),
         _ptr(value_cache), _ptr(slot_mapping), slot_mapping.numel(), nb, bs, hkv, d,
-        _code(key_cache.dtype), _stream(stream)))
+        _code(key.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
 
 
 def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
@@ -130,7 +136,9 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        window_left: int = -1, softcap: float = 0.0,
                        alibi_slopes: Optional[torch.Tensor] = None,
                        lse: Optional[torch.Tensor] = None, stream=None,
-                       sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       sinks: Optional[torch.Tensor] = None,
+                       k_scale: Optional[torch.Tensor] = None,
+                       v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     total_q, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     _check("paged_attn_prefill", lib.paged_attn_prefill(
@@ -138,7 +146,7 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), seq_lens.numel(), total_q,
         int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
         int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks), _code(q.dtype),
-        _stream(stream)))
+        _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
     return out
 
 
@@ -150,14 +158,17 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
                       part_out: Optional[torch.Tensor] = None,
                       part_lse: Optional[torch.Tensor] = None,
                       lse: Optional[torch.Tensor] = None, stream=None,
-                      sinks: Optional[torch.Tensor] = None) -> None:
+                      sinks: Optional[torch.Tensor] = None,
+                      k_scale: Optional[torch.Tensor] = None,
+                      v_scale: Optional[torch.Tensor] = None) -> None:
     b, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse), _ptr(q), _ptr(key_cache),
         _ptr(value_cache), _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b,
         int(max_seq_len), hq, hkv, d, bs, nb, float(scale), int(window_left), float(softcap),
-        _ptr(alibi_slopes), _ptr(sinks), int(num_splits), _code(q.dtype), _stream(stream)))
+        _ptr(alibi_slopes), _ptr(sinks), int(num_splits), _code(q.dtype), _code(key_cache.dtype),
+        _ptr(k_scale), _ptr(v_scale), _stream(stream)))
 
 
 def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: torch.Tensor,
@@ -176,7 +187,9 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        max_seqlen_k: int, scale: float, common_prefix_len: int,
                        softcap: float = 0.0, lse: Optional[torch.Tensor] = None,
                        max_prefix_splits: int = 16, workspace=None, stream=None,
-                       sinks: Optional[torch.Tensor] = None) -> None:
+                       sinks: Optional[torch.Tensor] = None,
+                       k_scale: Optional[torch.Tensor] = None,
+                       v_scale: Optional[torch.Tensor] = None) -> None:
     """Causal prefill over a shared prefix (see paged_attn_cascade in the
     header).  ``workspace`` is (parts_out, parts_lse, work_ints) sized for
     max_prefix_splits + 1 parts; it is allocated here with torch when not
@@ -195,8 +208,7 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b, t, int(max_seqlen_q),
         int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), float(softcap), _ptr(sinks),
         int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), _ptr(ints),
-        _code(q.dtype),
-        _stream(stream)))
+        _code(q.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
 
 
 def local_virtual_batches(attn_chunk_size: int, query_start_loc, seq_lens, block_table,

@@ -84,6 +84,21 @@ int check_attn_common(const char* fn, int num_seqs, int num_heads, int num_kv_he
   return PA_OK;
 }
 
+// the cache element type: the 16-bit dtype itself, or fp8 codes with their
+// device scales
+int check_kv(const char* fn, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype, const float* k_scale,
+             const float* v_scale, bool fp8_supported) {
+  if (kv_cache_dtype == dtype) return PA_OK;
+  if (kv_cache_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "%s: kv_cache_dtype must be dtype or PA_FP8_E4M3 (got %d)",
+                fn, (int)kv_cache_dtype);
+  if (!fp8_supported)
+    return fail(PA_ERR_UNSUPPORTED, "%s: an fp8 cache is not supported by this entry point", fn);
+  if (k_scale == nullptr || v_scale == nullptr)
+    return fail(PA_ERR_INVALID, "%s: an fp8 cache needs k_scale and v_scale", fn);
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,9 +109,12 @@ int reshape_and_cache(const void* key, const void* value, int64_t key_token_stri
                       int64_t value_token_stride, void* key_cache, void* value_cache,
                       const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
                       int block_size, int num_kv_heads, int head_size, pa_dtype_t dtype,
+                      pa_dtype_t kv_cache_dtype, const float* k_scale, const float* v_scale,
                       void* stream) {
   const char* fn = "reshape_and_cache";
   int rc = check_cache_shape(fn, block_size, num_kv_heads, head_size, dtype);
+  if (rc != PA_OK) return rc;
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
   if (rc != PA_OK) return rc;
   if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: num_tokens must be >= 0", fn);
   if (num_tokens == 0) return ok();
@@ -108,6 +126,13 @@ int reshape_and_cache(const void* key, const void* value, int64_t key_token_stri
     return fail(PA_ERR_INVALID, "%s: token strides (%lld, %lld) must be >= num_kv_heads*head_size (%lld)",
                 fn, (long long)key_token_stride, (long long)value_token_stride, (long long)row);
   if (num_blocks <= 0) return fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
+  if (kv_cache_dtype == PA_FP8_E4M3)
+    return hip_result(pa::launch_reshape_and_cache_fp8(
+                          key, value, key_token_stride, value_token_stride, key_cache,
+                          value_cache, slot_mapping, num_tokens, static_cast<int>(row),
+                          static_cast<pa::Dtype>(dtype), k_scale, v_scale,
+                          static_cast<hipStream_t>(stream)),
+                      fn);
   return hip_result(pa::launch_reshape_and_cache(key, value, key_token_stride, value_token_stride,
                                                  key_cache, value_cache, slot_mapping, num_tokens,
                                                  static_cast<int>(row),
@@ -122,11 +147,14 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
                        int max_seqlen_q, int max_seqlen_k, int num_heads, int num_kv_heads,
                        int head_size, int block_size, int64_t num_blocks, float scale, int causal,
                        int window_left, float softcap, const float* alibi_slopes,
-                       const float* sinks, pa_dtype_t dtype, void* stream) {
+                       const float* sinks, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
+                       const float* k_scale, const float* v_scale, void* stream) {
   const char* fn = "paged_attn_prefill";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, window_left, softcap, dtype, q, key_cache,
                              value_cache, seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, false);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -177,11 +205,14 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
                       int max_seq_len, int num_heads, int num_kv_heads, int head_size,
                       int block_size, int64_t num_blocks, float scale, int window_left,
                       float softcap, const float* alibi_slopes, const float* sinks,
-                      int num_splits, pa_dtype_t dtype, void* stream) {
+                      int num_splits, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
+                      const float* k_scale, const float* v_scale, void* stream) {
   const char* fn = "paged_attn_decode";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, window_left, softcap, dtype, q, key_cache,
                              value_cache, seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
   if (rc != PA_OK) return rc;
   if (num_splits < 1 || num_splits > 256)
     return fail(PA_ERR_INVALID, "%s: num_splits must be in [1, 256] (got %d)", fn, num_splits);
@@ -222,6 +253,9 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
   p.sinks = sinks;
   p.num_splits = num_splits;
   p.dtype = static_cast<pa::Dtype>(dtype);
+  p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -257,11 +291,14 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
                        float softcap, const float* sinks, int common_prefix_len,
                        int max_prefix_splits,
                        void* parts_out, float* parts_lse, int32_t* work_ints, pa_dtype_t dtype,
+                       pa_dtype_t kv_cache_dtype, const float* k_scale, const float* v_scale,
                        void* stream) {
   const char* fn = "paged_attn_cascade";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, -1, softcap, dtype, q, key_cache, value_cache,
                              seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, false);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)

@@ -41,6 +41,16 @@ struct BF16 {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf2));
   }
+  // four fp8 (OCP e4m3) codes, byte i -> element i; exact (every e4m3
+  // value is a bf16 value); one v_cvt_scalef32_pk_bf16_fp8 per pair, scale 1
+  static __device__ __forceinline__ v4s from_fp8x4(uint32_t w) {
+    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    // (whole registers: extracting the 16-bit lanes one by one made the
+    // compiler duplicate the low lane)
+    return __builtin_bit_cast(
+        v4s, (u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)}));
+  }
   // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 with (1, 1))
   static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pair),
@@ -65,6 +75,16 @@ struct BF16 {
 struct F16 {
   static __device__ __forceinline__ float to_float(uint16_t x) {
     return static_cast<float>(__builtin_bit_cast(_Float16, x));
+  }
+  // four fp8 (OCP e4m3) codes, byte i -> element i; exact (every e4m3
+  // value is an fp16 value); one v_cvt_scalef32_pk_f16_fp8 per pair, scale 1
+  static __device__ __forceinline__ v4s from_fp8x4(uint32_t w) {
+    const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+    // (whole registers: extracting the 16-bit lanes one by one made the
+    // compiler duplicate the low lane)
+    return __builtin_bit_cast(
+        v4s, (u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)}));
   }
   static __device__ __forceinline__ uint16_t from_float(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));

@@ -24,6 +24,8 @@
 // online-softmax state (fp32, base-2 exponent) and are merged through LDS at
 // the item's end.  The loads of a wave's next step are issued before its
 // current step is computed.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -55,9 +57,13 @@ struct DecodeArgs {
   // attention sinks [Hq] (fp32, nullable): one more logit per head in the
   // softmax denominator, without a value; folded into split 0 only
   const float* sinks;
+  // fp8 (e4m3) cache: device fp32 scales (the stored codes times the scale
+  // are the K / V values); null for a 16-bit cache
+  const float* k_scale;
+  const float* v_scale;
 };
 
-enum { kSoftcap = 1, kAlibi = 2 };
+enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4 };
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // A work item covers HPW adjacent KV heads (2 when the head counts allow it
@@ -114,17 +120,44 @@ template <typename T, int D, int FEAT, int HPW>
 struct Dec {
   static constexpr bool SOFTCAP = FEAT & kSoftcap;
   static constexpr bool ALIBI = FEAT & kAlibi;
+  static constexpr bool F8 = FEAT & kFp8;
   static constexpr int KK = D / 32;   // QK mfma steps along D
+  static constexpr int NU = D / 64;   // fp8: 16-byte pieces of a row per lane
   static constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
   static constexpr int NT = kNT<D, HPW>;
   static constexpr int KPS = 16 * NT; // keys per step
   static constexpr int P = kVPitch<D, HPW>;
   static constexpr int CP = D + 4;    // combine row: m, l, 2 pad, O[D] (16-byte aligned)
 
-  struct Frag {
+  // 16-bit cache: lane (r16, c4) holds elements kk*32 + 8*c4 + [0, 8) of
+  // key row r16 for each QK step kk.  fp8 cache: it holds bytes
+  // u*64 + 16*c4 + [0, 16) (16-byte loads, half the bytes); QK step kk then
+  // contracts elements (kk/2)*64 + 16*c4 + 8*(kk%2) + [0, 8), and load_q
+  // takes Q in the same order (a permutation of the sum over d).
+  struct Frag16 {
     v8s k[HPW][NT][KK];
     v8s v[HPW][NT][KK];
   };
+  struct Frag8 {
+    u32x4 k[HPW][NT][NU];
+    u32x4 v[HPW][NT][NU];
+  };
+  using Frag = std::conditional_t<F8, Frag8, Frag16>;
+  // element offset of this lane's 8 Q / K elements of QK step kk
+  static __device__ __forceinline__ int qk_off(int kk, int c4) {
+    return F8 ? (kk >> 1) * 64 + 16 * c4 + 8 * (kk & 1) : kk * 32 + 8 * c4;
+  }
+  // the 16-bit K operand of QK step kk
+  static __device__ __forceinline__ v8s k_operand(const Frag& f, int h, int nt, int kk) {
+    if constexpr (F8) {
+      const u32x4& w = f.k[h][nt][kk >> 1];
+      const v4s lo = T::from_fp8x4(w[2 * (kk & 1)]);
+      const v4s hi = T::from_fp8x4(w[2 * (kk & 1) + 1]);
+      return v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return f.k[h][nt][kk];
+    }
+  }
 
   // KV heads g0 .. g0 + HPW - 1 of sequence b, keys [lo_vis, hi) of `split`
   struct Item {
@@ -170,6 +203,26 @@ struct Dec {
                                                    const int (&ids)[NT], int r16, int c4,
                                                    Frag& f) {
     const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive slots
+    if constexpr (F8) {
+      const uint8_t* kcg = reinterpret_cast<const uint8_t*>(a.kc) + (int64_t)it.g0 * D + c4 * 16;
+      const uint8_t* vcg = reinterpret_cast<const uint8_t*>(a.vc) + (int64_t)it.g0 * D + c4 * 16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int j0 = tile_j0(it, step, nt);
+        const int q = div_magic(j0, a.bs_magic);
+        const int64_t slot = (int64_t)ids[nt] * a.bs + (j0 - q * a.bs) + r16;
+        const uint8_t* kp = kcg + slot * row_stride;
+        const uint8_t* vp = vcg + slot * row_stride;
+#pragma unroll
+        for (int h = 0; h < HPW; ++h)
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            f.k[h][nt][u] = *reinterpret_cast<const u32x4*>(kp + h * D + u * 64);
+            f.v[h][nt][u] = *reinterpret_cast<const u32x4*>(vp + h * D + u * 64);
+          }
+      }
+      return;
+    } else {
     const uint16_t* kcg = a.kc + (int64_t)it.g0 * D + c4 * 8;
     const uint16_t* vcg = a.vc + (int64_t)it.g0 * D + c4 * 8;
 #pragma unroll
@@ -187,6 +240,7 @@ struct Dec {
           f.v[h][nt][kk] = *reinterpret_cast<const v8s*>(vp + h * D + kk * 32);
         }
     }
+    }
   }
 
   // The Q row of this lane's column (head g0 * G + r16; padding columns load
@@ -194,9 +248,9 @@ struct Dec {
   static __device__ __forceinline__ void load_q(const DecodeArgs& a, const Item& it, int r16,
                                                 int c4, v8s (&qraw)[KK]) {
     const int hq = it.g0 * a.G + (r16 < a.G * HPW ? r16 : 0);
-    const uint16_t* qrow = a.q + ((int64_t)it.b * a.Hq + hq) * D + c4 * 8;
+    const uint16_t* qrow = a.q + ((int64_t)it.b * a.Hq + hq) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const v8s*>(qrow + kk * 32);
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const v8s*>(qrow + qk_off(kk, c4));
   }
   // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8; with two
   // KV heads, operand h is zero outside head h's columns, so the two products
@@ -236,7 +290,7 @@ struct Dec {
 #pragma unroll
       for (int h = 0; h < HPW; ++h)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc = T::mfma16x16x32(f.k[h][nt][kk], qf[h][kk], sc);
+        for (int kk = 0; kk < KK; ++kk) sc = T::mfma16x16x32(k_operand(f, h, nt, kk), qf[h][kk], sc);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = j0 + 4 * c4 + e;
@@ -281,14 +335,31 @@ struct Dec {
     for (int nt = 0; nt < NT; ++nt) {
       const int key = step * KPS + 16 * nt + r16;
       const bool row_ok = key >= it.lo_vis && key < it.hi;
-      uint16_t* dst = vs + (16 * nt + r16) * P + c4 * 8;
+      const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (F8) {
+        // the row's bytes u*64 + 16*c4 + [0, 16) become elements at the same
+        // positions of the LDS row
+        uint16_t* dst = vs + (16 * nt + r16) * P + c4 * 16;
 #pragma unroll
-      for (int h = 0; h < HPW; ++h)
+        for (int h = 0; h < HPW; ++h)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
-          *reinterpret_cast<v8s*>(dst + h * D + kk * 32) = row_ok ? f.v[h][nt][kk] : z;
-        }
+          for (int u = 0; u < NU; ++u) {
+            const u32x4& w = f.v[h][nt][u];
+            const v4s e0 = T::from_fp8x4(w[0]), e1 = T::from_fp8x4(w[1]);
+            const v4s e2 = T::from_fp8x4(w[2]), e3 = T::from_fp8x4(w[3]);
+            const v8s lo = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+            const v8s hi = {e2[0], e2[1], e2[2], e2[3], e3[0], e3[1], e3[2], e3[3]};
+            *reinterpret_cast<v8s*>(dst + h * D + u * 64) = row_ok ? lo : z;
+            *reinterpret_cast<v8s*>(dst + h * D + u * 64 + 8) = row_ok ? hi : z;
+          }
+      } else {
+        uint16_t* dst = vs + (16 * nt + r16) * P + c4 * 8;
+#pragma unroll
+        for (int h = 0; h < HPW; ++h)
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            *reinterpret_cast<v8s*>(dst + h * D + kk * 32) = row_ok ? f.v[h][nt][kk] : z;
+      }
     }
     wave_lds_sync();
     // ---- O^T[d][head] += V^T[d][key] P^T[key][head]; lane group c4 reads
@@ -393,7 +464,8 @@ struct Dec {
           num += fw * *reinterpret_cast<const v4f*>(comb + (w * GC + j) * CP + 4 + d);
         }
       }
-      const float inv = den > 0.f ? 1.0f / den : 0.f;
+      // (an fp8 cache's V scale multiplies the result)
+      const float inv = den > 0.f ? (F8 ? *a.v_scale : 1.0f) / den : 0.f;
       const float lse = den > 0.f ? (M + __log2f(den)) * kLn2 : kNegInf;
       emit4(a, it.g0, it.b, it.split, j, d, num * inv, lse);
     }
@@ -411,6 +483,12 @@ template <typename T, int D, int FEAT, int HPW>
 __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(DecodeArgs a) {
   using K = Dec<T, D, FEAT, HPW>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  if constexpr (K::F8) {
+    // the K scale multiplies every score
+    const float ks = *a.k_scale;
+    a.scale_log2 *= ks;
+    a.scale_over_cap *= ks;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -489,20 +567,20 @@ int launch_d(const DecodeArgs& args, hipStream_t stream) {
   return launch_h<T, D, FEAT, 1>(args, stream);
 }
 
-template <typename T, int D>
+template <typename T, int D, int F8>
 int launch_feat(const DecodeArgs& a, bool softcap, bool alibi, hipStream_t s) {
-  if (softcap && alibi) return launch_d<T, D, kSoftcap | kAlibi>(a, s);
-  if (softcap) return launch_d<T, D, kSoftcap>(a, s);
-  if (alibi) return launch_d<T, D, kAlibi>(a, s);
-  return launch_d<T, D, 0>(a, s);
+  if (softcap && alibi) return launch_d<T, D, F8 | kSoftcap | kAlibi>(a, s);
+  if (softcap) return launch_d<T, D, F8 | kSoftcap>(a, s);
+  if (alibi) return launch_d<T, D, F8 | kAlibi>(a, s);
+  return launch_d<T, D, F8>(a, s);
 }
 
-template <typename T>
+template <typename T, int F8>
 int launch_t(const DecodeArgs& a, int D, bool softcap, bool alibi, hipStream_t s) {
   switch (D) {
-    case 64: return launch_feat<T, 64>(a, softcap, alibi, s);
-    case 128: return launch_feat<T, 128>(a, softcap, alibi, s);
-    default: return launch_feat<T, 256>(a, softcap, alibi, s);
+    case 64: return launch_feat<T, 64, F8>(a, softcap, alibi, s);
+    case 128: return launch_feat<T, 128, F8>(a, softcap, alibi, s);
+    default: return launch_feat<T, 256, F8>(a, softcap, alibi, s);
   }
 }
 
@@ -540,9 +618,15 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;
   a.sinks = p.sinks;
+  a.k_scale = p.k_scale;
+  a.v_scale = p.v_scale;
   const bool alibi = p.alibi_slopes != nullptr;
-  if (p.dtype == kBF16) return launch_t<BF16>(a, p.head_size, softcap, alibi, stream);
-  return launch_t<F16>(a, p.head_size, softcap, alibi, stream);
+  if (p.kv_fp8) {
+    if (p.dtype == kBF16) return launch_t<BF16, kFp8>(a, p.head_size, softcap, alibi, stream);
+    return launch_t<F16, kFp8>(a, p.head_size, softcap, alibi, stream);
+  }
+  if (p.dtype == kBF16) return launch_t<BF16, 0>(a, p.head_size, softcap, alibi, stream);
+  return launch_t<F16, 0>(a, p.head_size, softcap, alibi, stream);
 }
 
 }  // namespace pa

@@ -14,6 +14,13 @@ int launch_reshape_and_cache(const void* key, const void* value, int64_t key_str
                              const int64_t* slots, int64_t num_tokens, int row_elems,
                              hipStream_t stream);
 
+// fp8 (e4m3) cache: in_dtype kF16 / kBF16 inputs, device fp32 scales
+int launch_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_stride,
+                                 int64_t value_stride, void* key_cache, void* value_cache,
+                                 const int64_t* slots, int64_t num_tokens, int row_elems,
+                                 Dtype in_dtype, const float* k_scale, const float* v_scale,
+                                 hipStream_t stream);
+
 int launch_merge(void* out, float* out_lse, const void* parts, const float* parts_lse,
                  int num_parts, int64_t num_tokens, int num_heads, int head_size,
                  Dtype parts_dtype, Dtype out_dtype, hipStream_t stream);
@@ -44,6 +51,9 @@ struct AttnParams {
   float softcap;
   const float* alibi_slopes;
   const float* sinks;  // [Hq] fp32 attention-sink logits or null; split 0 only
+  int kv_fp8;          // nonzero: the caches hold fp8 (e4m3) codes
+  const float* k_scale;  // fp8 cache: device fp32 scales
+  const float* v_scale;
   int num_splits;
   int key_split;  // prefill only: keys per split (a multiple of 64), 0 = none
   Dtype dtype;

@@ -42,7 +42,8 @@ def lib():
 def _decode(pa, **kw):
     args = dict(out=1, lse=None, part_out=None, part_lse=None, q=1, kc=1, vc=1, seq_lens=1,
                 bt=1, bt_stride=4, num_seqs=2, max_seq_len=10, hq=4, hkv=2, d=64, bs=16, nb=8,
-                scale=0.125, wl=-1, cap=0.0, alibi=None, sinks=None, splits=1, dtype=pa.PA_F16)
+                scale=0.125, wl=-1, cap=0.0, alibi=None, sinks=None, splits=1, dtype=pa.PA_F16,
+                kvdt=pa.PA_F16, ks=None, vs=None)
     args.update(kw)
     return pa.lib.paged_attn_decode(*args.values(), None)
 
@@ -50,7 +51,8 @@ def _decode(pa, **kw):
 def _prefill(pa, **kw):
     args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
                 num_seqs=1, total_q=5, mq=5, mk=23, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
-                causal=1, wl=-1, cap=0.0, alibi=None, sinks=None, dtype=pa.PA_F16)
+                causal=1, wl=-1, cap=0.0, alibi=None, sinks=None, dtype=pa.PA_F16,
+                kvdt=pa.PA_F16, ks=None, vs=None)
     args.update(kw)
     return pa.lib.paged_attn_prefill(*args.values(), None)
 
@@ -76,6 +78,17 @@ def test_prefill_validation(lib, kw, code):
     assert _prefill(lib, **kw) == code
 
 
+def test_fp8_cache_validation(lib):
+    F8 = lib.PA_FP8_E4M3
+    assert _decode(lib, kvdt=F8, ks=None, vs=1) == -1          # scales required
+    assert _decode(lib, kvdt=F8, ks=1, vs=None) == -1
+    assert _decode(lib, kvdt=lib.PA_BF16) == -2                 # cache type must match q
+    assert _decode(lib, kvdt=9, ks=1, vs=1) == -2
+    assert _prefill(lib, kvdt=F8, ks=1, vs=1) == -2             # prefill reads 16-bit caches
+    assert _cascade(lib, kvdt=F8, ks=1, vs=1) == -2
+    assert lib.pa_last_error().startswith("paged_attn_cascade")
+
+
 def test_empty_calls_are_noops(lib):
     assert _decode(lib, num_seqs=0, q=None, kc=None, vc=None, seq_lens=None, bt=None) == 0
     assert _prefill(lib, num_seqs=0, q=None, kc=None, vc=None, seq_lens=None, bt=None, cu=None,
@@ -85,11 +98,18 @@ def test_empty_calls_are_noops(lib):
 
 def test_reshape_and_cache_validation(lib):
     f = lib.lib.reshape_and_cache
-    assert f(1, 1, 100, 128, 1, 1, 1, 4, 8, 16, 2, 64, lib.PA_BF16, None) == -1   # short stride
-    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 20, 2, 64, lib.PA_BF16, None) == -1   # block size
-    assert f(1, 1, 128, 128, 1, 1, None, 4, 8, 16, 2, 64, lib.PA_BF16, None) == -1
-    assert f(None, None, 128, 128, None, None, None, 0, 8, 16, 2, 64, lib.PA_BF16, None) == 0
-    assert f(1, 1, 128, 128, 1, 1, 1, -1, 8, 16, 2, 64, lib.PA_BF16, None) == -1
+    B = lib.PA_BF16
+    assert f(1, 1, 100, 128, 1, 1, 1, 4, 8, 16, 2, 64, B, B, None, None, None) == -1  # short stride
+    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 20, 2, 64, B, B, None, None, None) == -1  # block size
+    assert f(1, 1, 128, 128, 1, 1, None, 4, 8, 16, 2, 64, B, B, None, None, None) == -1
+    assert f(None, None, 128, 128, None, None, None, 0, 8, 16, 2, 64, B, B, None, None, None) == 0
+    assert f(1, 1, 128, 128, 1, 1, 1, -1, 8, 16, 2, 64, B, B, None, None, None) == -1
+    # fp8 cache: scales required; the cache type is dtype or fp8
+    F8 = lib.PA_FP8_E4M3
+    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 16, 2, 64, B, F8, None, 1, None) == -1
+    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 16, 2, 64, B, F8, 1, None, None) == -1
+    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 16, 2, 64, B, lib.PA_F16, None, None, None) == -2
+    assert f(1, 1, 128, 128, 1, 1, 1, 4, 8, 16, 2, 64, F8, F8, 1, 1, None) == -2
 
 
 def test_merge_validation(lib):
@@ -118,7 +138,8 @@ def test_check_indices_validation(lib):
 def _cascade(pa, **kw):
     args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
                 num_seqs=2, total_q=5, mq=3, mk=80, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
-                cap=0.0, sinks=None, prefix=32, max_splits=4, parts=1, parts_lse=1, ints=1, dtype=pa.PA_BF16)
+                cap=0.0, sinks=None, prefix=32, max_splits=4, parts=1, parts_lse=1, ints=1, dtype=pa.PA_BF16,
+                kvdt=pa.PA_BF16, ks=None, vs=None)
     args.update(kw)
     return pa.lib.paged_attn_cascade(*args.values(), None)
 

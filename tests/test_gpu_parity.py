@@ -77,10 +77,11 @@ def test_reshape_and_cache_padding_strides_negative_slots(pa, dtype, D, Hkv, ali
     kdev, vdev = kbig.cuda(), vbig.cuda()
     kview = kdev[:, :row]
     vview = vdev[:, pad:pad + row]
+    code = pa.PA_F16 if dtype == torch.float16 else pa.PA_BF16
     rc = pa.lib.reshape_and_cache(kview.data_ptr(), vview.data_ptr(), kview.stride(0),
                                   vview.stride(0), kd.data_ptr(), vd.data_ptr(),
                                   slots.cuda().data_ptr(), T, nb, bs, Hkv, D,
-                                  pa.PA_F16 if dtype == torch.float16 else pa.PA_BF16,
+                                  code, code, None, None,
                                   torch.cuda.current_stream().cuda_stream)
     assert rc == 0, pa.pa_last_error()
     torch.cuda.synchronize()
