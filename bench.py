@@ -10,6 +10,9 @@ Inputs are seeded synthetic data resident in HBM before timing starts.  Each
 step uses the next of `--layers` independent caches (as consecutive layers of
 a model would) so no step re-reads K/V another step left in the caches.
 
+`--kv-fp8` runs the decode workloads over an fp8 (e4m3) cache with
+per-tensor scales (the bytes then count one byte per element).
+
 Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on a
 single GPU.
 """
@@ -45,9 +48,13 @@ def visible_keys(L: int, pos: int, causal: bool, window_left: int) -> int:
     return max(0, hi - lo)
 
 
-def decode_bytes(w, call) -> int:
+# per-tensor scales of the fp8 (e4m3) cache in --kv-fp8 runs: the largest
+# |x| of N(0,1) data over a few million draws (about 5.6) maps to 448
+FP8_SCALES = (5.6 / 448.0, 5.6 / 448.0)
+
+
+def decode_bytes(w, call, elem: int = 2) -> int:
     """K and V bytes every decode query must see: visible keys x Hkv x D x 2 x elem."""
-    elem = 2
     keys = sum(visible_keys(int(L), int(L) - 1, True, w.window_left) for L in call.seq_lens)
     return keys * w.num_kv_heads * w.head_size * 2 * elem
 
@@ -106,7 +113,7 @@ class Timed:
 
 def run_decode(args, pa, runner, w):
     call = w.steps[0].calls[0]
-    base = runner.PagedCache(w)
+    base = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
     base.fill_context()
     caches = [base]
     for _ in range(args.layers - 1):
@@ -127,9 +134,9 @@ def run_decode(args, pa, runner, w):
         c, cb = caches[i % len(caches)], bufs[i % len(caches)]
         if timed:
             with rac_t:
-                pa.reshape_and_cache(k, v, c.key_cache, c.value_cache, s)
+                c.write(k, v, s)
         else:
-            pa.reshape_and_cache(k, v, c.key_cache, c.value_cache, s)
+            c.write(k, v, s)
         if cb.num_splits == 1:
             if timed:
                 with dec_t:
@@ -137,7 +144,8 @@ def run_decode(args, pa, runner, w):
             else:
                 c.run(cb)
             return
-        kw = dict(part_out=cb.part_out, part_lse=cb.part_lse)
+        kw = dict(part_out=cb.part_out, part_lse=cb.part_lse, k_scale=c.k_scale,
+                  v_scale=c.v_scale)
         if timed:
             with dec_t:
                 pa.paged_attn_decode(None, cb.q, c.key_cache, c.value_cache, cb.seq_lens,
@@ -164,7 +172,7 @@ def run_decode(args, pa, runner, w):
     for i in range(args.steps):
         step(i, True)
     torch.cuda.synchronize()
-    nbytes = decode_bytes(w, call)
+    nbytes = decode_bytes(w, call, 1 if args.kv_fp8 else 2)
     return dict(ms_per_step=wall_ms, decode_ms=dec_t.mean_ms(), rac_ms=rac_t.mean_ms(),
                 merge_ms=merge_t.mean_ms() if merge_t.pairs else 0.0, bytes=nbytes,
                 tokens=int(s.numel()))
@@ -435,6 +443,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sinks", action="store_true",
                     help="decode/mixed/long: pass per-head attention-sink logits")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="decode/mixed/long: fp8 (e4m3) K/V cache with per-tensor scales")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -478,9 +488,11 @@ def main():
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 K/V cache, bf16 q" if args.kv_fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": call.num_seqs,
+        "config": {"workload": w.name + ("_kvfp8" if args.kv_fp8 else ""),
+                   "num_seqs": call.num_seqs,
                    "context_tokens": int(call.seq_lens.sum()), "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
                    "block_size": w.block_size, "num_splits": args.splits,
@@ -491,12 +503,14 @@ def main():
                        "merge_attn_states": round(r["merge_ms"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(f"decode:{w.name}:S{args.splits}", digest),
+                     "traffic": traffic_from_profile(
+                         f"decode:{w.name}{'_kvfp8' if args.kv_fp8 else ''}:S{args.splits}",
+                         digest),
                      "kernel": "paged_attn_decode", "bytes_per_launch": r["bytes"]},
     }
     if not args.no_prefill and args.workload == "decode":
         out["prefill"] = run_prefill(args, pa, runner)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.kv_fp8:
         sk = bench_sinks(args, w)
         out["cpu_baseline"] = cpu_baseline(w, sinks=None if sk is None else sk.cpu())
     print(json.dumps(out), flush=True)

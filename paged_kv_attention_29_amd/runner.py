@@ -35,21 +35,31 @@ class CallBuffers:
 
 
 class PagedCache:
-    """One layer's K/V cache for a workload."""
+    """One layer's K/V cache for a workload.  With ``kv_scales = (k_scale,
+    v_scale)`` the cache holds fp8 (e4m3) codes written by the quantising
+    reshape_and_cache with those per-tensor scales (unwritten slots hold the
+    NaN code 0x7F); otherwise it holds the workload's 16-bit dtype."""
 
-    def __init__(self, w, device: str = "cuda"):
+    def __init__(self, w, device: str = "cuda", kv_scales=None):
         self.w = w
         self.device = device
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
-        self.key_cache = torch.full(shape, float("nan"), dtype=w.dtype, device=device)
-        self.value_cache = torch.full(shape, float("nan"), dtype=w.dtype, device=device)
+        if kv_scales is None:
+            self.key_cache = torch.full(shape, float("nan"), dtype=w.dtype, device=device)
+            self.k_scale = self.v_scale = None
+        else:
+            self.key_cache = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
+            self.k_scale = torch.tensor([float(kv_scales[0])], device=device)
+            self.v_scale = torch.tensor([float(kv_scales[1])], device=device)
+        self.value_cache = self.key_cache.clone()
         self.block_table = torch.from_numpy(w.block_table).to(device)
         self.alibi = None if w.alibi_slopes is None else w.alibi_slopes.to(device)
         self.sinks = None  # optional fp32 [num_heads] attention-sink logits on the device
 
     def write(self, key: torch.Tensor, value: torch.Tensor, slots: torch.Tensor) -> None:
         reshape_and_cache(key.to(self.device), value.to(self.device), self.key_cache,
-                          self.value_cache, slots.to(self.device))
+                          self.value_cache, slots.to(self.device), k_scale=self.k_scale,
+                          v_scale=self.v_scale)
 
     def fill_context(self) -> None:
         for _, k, v, s in self.w.context_tokens():
@@ -86,16 +96,19 @@ class PagedCache:
             paged_attn_prefill(cb.out, cb.q, self.key_cache, self.value_cache, cb.cu_seqlens_q,
                                cb.seq_lens, cb.block_table, cb.max_seqlen_q, cb.max_seqlen_k,
                                w.scale, True, w.window_left, w.softcap, self.alibi, lse=cb.lse,
-                               stream=stream, sinks=self.sinks)
+                               stream=stream, sinks=self.sinks, k_scale=self.k_scale,
+                               v_scale=self.v_scale)
         elif cb.num_splits == 1:
             paged_attn_decode(cb.out, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
-                              self.alibi, 1, lse=cb.lse, stream=stream, sinks=self.sinks)
+                              self.alibi, 1, lse=cb.lse, stream=stream, sinks=self.sinks,
+                              k_scale=self.k_scale, v_scale=self.v_scale)
         else:
             paged_attn_decode(None, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
                               self.alibi, cb.num_splits, part_out=cb.part_out,
-                              part_lse=cb.part_lse, stream=stream, sinks=self.sinks)
+                              part_lse=cb.part_lse, stream=stream, sinks=self.sinks,
+                              k_scale=self.k_scale, v_scale=self.v_scale)
             merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse, stream=stream)
 
 
@@ -106,7 +119,7 @@ def run_workload(w, num_splits: Optional[int] = None, device: str = "cuda"):
     results: List[List[CallBuffers]] = []
     for step in w.steps:
         k, v, s = cache.step_inputs(step)
-        reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+        cache.write(k, v, s)
         bufs = [cache.call_buffers(c, num_splits) for c in step.calls]
         for cb in bufs:
             cache.run(cb)
