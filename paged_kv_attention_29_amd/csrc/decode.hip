@@ -90,11 +90,21 @@ template <int D, int HPW>
 constexpr size_t comb_bytes(int G) {
   return (size_t)kWaves * G * HPW * (D + 4) * 4;
 }
-// the combine runs after the key loop and reuses the V slabs
+// The combine runs after the key loop and reuses the V slabs.  The
+// work-item ranking runs before both (scratch ints at the start, below) and
+// hands its result over in a 16-byte slot past the slabs, the combine area
+// and the scratch, which nothing else writes.
+constexpr size_t kRankScratchBytes = (64 + 1 + 1024) * 4;
+template <int D, int HPW>
+constexpr size_t rank_slot_offset(int G) {
+  const size_t vc = vslab_bytes<D, HPW>() > comb_bytes<D, HPW>(G) ? vslab_bytes<D, HPW>()
+                                                                   : comb_bytes<D, HPW>(G);
+  const size_t m = vc > kRankScratchBytes ? vc : kRankScratchBytes;
+  return (m + 15) / 16 * 16;
+}
 template <int D, int HPW>
 constexpr size_t decode_lds_bytes(int G) {
-  return vslab_bytes<D, HPW>() > comb_bytes<D, HPW>(G) ? vslab_bytes<D, HPW>()
-                                                        : comb_bytes<D, HPW>(G);
+  return rank_slot_offset<D, HPW>(G) + 16;
 }
 
 template <int D>
@@ -113,6 +123,116 @@ __device__ __forceinline__ SplitRange split_range(const DecodeArgs& a, int L, in
   r.hi = p == a.S - 1 ? L : min(r.lo + a.chunk, L);
   r.lo_vis = a.window_left >= 0 ? max(r.lo, L - 1 - a.window_left) : r.lo;
   return r;
+}
+
+// Splits pf..pl of a sequence of L > 0 keys have visible keys (split_range
+// gives lo_vis < hi exactly for these; a zero chunk leaves every key to the
+// last split).
+__device__ __forceinline__ void split_span(const DecodeArgs& a, int L, int& pf, int& pl) {
+  const int lw = a.window_left >= 0 ? max(L - 1 - a.window_left, 0) : 0;
+  pf = a.chunk > 0 ? min(lw / a.chunk, a.S - 1) : a.S - 1;
+  pl = a.chunk > 0 ? min((L - 1) / a.chunk, a.S - 1) : a.S - 1;
+}
+
+// Work-item order for batches of at most kRankMaxB sequences and kRankMaxS
+// splits: workgroup i takes the i-th item of the list "every (sequence,
+// split) pair with visible keys, split-major, sequences in index order,
+// KV-head groups fastest; then the empty pairs in the same order".  Empty
+// items only write their zero / -inf result, but each still holds a
+// workgroup slot while it waits for its sequence length behind the loads in
+// flight; listed last, they run while the last real items finish instead of
+// taking slots between them.  Wave 0 of every workgroup derives the order
+// from seq_lens (LDS scratch: the per-split difference counts and the
+// lengths) and hands the item to the other waves through a slot past the V
+// slabs and the combine area, so no pass runs before the kernel.  Other
+// batches use the plain split-major order.
+constexpr int kRankMaxB = 1024;
+constexpr int kRankMaxS = 64;
+static_assert((kRankMaxS + 1 + kRankMaxB) * 4 <= kRankScratchBytes, "ranking scratch size");
+
+struct ItemRef {
+  int g0, b, split, L;
+};
+
+// wave 0 only; sh = LDS scratch, res = the hand-off slot (4 ints)
+template <int HPW>
+__device__ void ranked_item_wave0(const DecodeArgs& a, int* sh, int* res) {
+  const int S = a.S, B = a.B, HG = a.Hkv / HPW;
+  const int lane = threadIdx.x & 63;
+  int* cnt = sh;                  // [S + 1] difference counts
+  int* lens = sh + kRankMaxS + 1; // [B]
+  if (lane <= S) cnt[lane] = 0;
+  if (lane == 0 && S == 64) cnt[64] = 0;
+  wave_lds_sync();
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    if (b < B) {
+      const int L = a.seq_lens[b];
+      lens[b] = L;
+      if (L > 0) {
+        int pf, pl;
+        split_span(a, L, pf, pl);
+        atomicAdd(cnt + pf, 1);
+        atomicAdd(cnt + pl + 1, -1);
+      }
+    }
+  }
+  wave_lds_sync();  // the adds of every lane land before the reads
+  const int d = lane < S ? cnt[lane] : 0;
+  // lane p: c = sequences with a non-empty split p, base = non-empty pairs
+  // of the splits before p
+  int run_c = 0, run_b = 0, base = 0;
+  for (int p = 0; p < S; ++p) {
+    run_c += __builtin_amdgcn_readlane(d, p);
+    base = lane == p ? run_b : base;
+    run_b += run_c;
+  }
+  const int total = run_b;
+  int idx = static_cast<int>(blockIdx.x);
+  const bool want = idx < total * HG;  // a non-empty item
+  if (!want) idx -= total * HG;
+  const int r = idx / HG;
+  const int g = idx - r * HG;
+  // the split: the last p whose list of items starts at or before r (the
+  // starts grow with p, so those p are a prefix of the lanes)
+  const int start = want ? base : lane * B - base;
+  const uint64_t before = __builtin_amdgcn_ballot_w64(lane < S && start <= r);
+  const int split = static_cast<int>(__builtin_popcountll(before)) - 1;
+  int rr = r - __builtin_amdgcn_readlane(start, split);
+  // the rr-th sequence, in index order, whose split is (non-)empty
+  int sel = -1;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    bool flag = false;
+    if (b < B) {
+      const int L = lens[b];
+      bool ne = false;
+      if (L > 0) {
+        int pf, pl;
+        split_span(a, L, pf, pl);
+        ne = pf <= split && split <= pl;
+      }
+      flag = ne == want;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(flag);
+    const int n = static_cast<int>(__builtin_popcountll(m));
+    if (rr < n) {
+      const int rank = static_cast<int>(__builtin_popcountll(m & ((1ull << lane) - 1)));
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(flag && rank == rr);
+      sel = b0 + static_cast<int>(__builtin_ctzll(hit));
+      break;
+    }
+    rr -= n;
+  }
+  // (every workgroup finds its item, since the grid holds exactly HG * B * S
+  // of them; sel < 0 would mean inconsistent lengths and makes the kernel
+  // exit)
+  if (lane == 0) {
+    res[0] = g * HPW;
+    res[1] = sel;
+    res[2] = split;
+    res[3] = sel >= 0 ? lens[sel] : 0;
+  }
 }
 
 // The pieces of one work item.
@@ -495,15 +615,28 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int r16 = lane & 15;   // key row of the K piece / head column of the tile
   const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
 
-  const int HG = a.Hkv / HPW;
-  const int per_split = HG * a.B;
-  const int split = blockIdx.x / per_split;
-  int j = blockIdx.x - split * per_split - static_cast<int>((int64_t)split * HG % per_split);
-  if (j < 0) j += per_split;
-  const int g0 = (j % HG) * HPW;  // first KV head of the item
-  const int b = j / HG;
+  int g0, b, split, L;
+  if (a.B <= kRankMaxB && a.S <= kRankMaxS) {
+    int* res = reinterpret_cast<int*>(smem + rank_slot_offset<D, HPW>(a.G));
+    if (wave == 0) ranked_item_wave0<HPW>(a, reinterpret_cast<int*>(smem), res);
+    __syncthreads();
+    g0 = __builtin_amdgcn_readfirstlane(res[0]);
+    b = __builtin_amdgcn_readfirstlane(res[1]);
+    split = __builtin_amdgcn_readfirstlane(res[2]);
+    L = __builtin_amdgcn_readfirstlane(res[3]);
+    if (b < 0) return;
+  } else {
+    const int HG = a.Hkv / HPW;
+    const int per_split = HG * a.B;
+    split = blockIdx.x / per_split;
+    int j = blockIdx.x - split * per_split - static_cast<int>((int64_t)split * HG % per_split);
+    if (j < 0) j += per_split;
+    g0 = (j % HG) * HPW;  // first KV head of the item
+    b = j / HG;
+    L = a.seq_lens[b];
+  }
 
-  const typename K::Item it = K::make_item(a, g0, b, split, a.seq_lens[b]);
+  const typename K::Item it = K::make_item(a, g0, b, split, L);
   if (it.lo_vis >= it.hi) {
     K::emit_empty(a, g0, b, split);
     return;

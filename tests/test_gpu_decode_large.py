@@ -67,6 +67,8 @@ LARGE = [
     ("two_heads_window", 300, 16, 4, 128, 16, 200, 0.0, False, 8),
     ("one_head_d64_cap_alibi", 260, 12, 3, 64, 32, -1, 30.0, True, 5),
     ("d256_unsplit", 600, 8, 1, 256, 16, -1, 0.0, False, 1),
+    # more than 64 splits: the plain split-major item order
+    ("many_splits", 70, 8, 2, 128, 16, -1, 0.0, False, 80),
 ]
 
 
