@@ -4,6 +4,8 @@
 // head_size / 64 consecutive output elements, so every part row is read
 // as one coalesced 64-lane access.  Memory-bound: it reads
 // num_parts * (head_size * elem + 4) bytes per (token, head).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -50,11 +52,25 @@ __global__ __launch_bounds__(256) void merge_kernel(void* __restrict__ out,
   const int64_t lse_stride = (int64_t)H * T;
   const int64_t lse_off = (int64_t)h * T + t;
 
-  float m = kNegInf;
-  for (int p = lane; p < S; p += 64) m = fmaxf(m, parts_lse[p * lse_stride + lse_off]);
+  const int64_t row = pair * D + lane * EPL;  // (t * H + h) * D
+  const int64_t part_stride = T * H * D;
+  // The LSEs of parts [0, 64) (lane p holds part p's) and the rows of the
+  // first batch of parts go out together: the row loads do not wait for the
+  // maximum, so up to eight parts cost one memory latency.
+  constexpr int NB = 8;
+  const int nb0 = S < NB ? S : NB;
+  const float lse_l = lane < S ? parts_lse[lane * lse_stride + lse_off] : kNegInf;
+  float x0[NB][EPL];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    if (j < nb0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x0[j][e] = Elem<PT>::ld(parts, j * part_stride + row + e);
+    }
+  float m = lse_l;
+  for (int p = 64 + lane; p < S; p += 64) m = fmaxf(m, parts_lse[p * lse_stride + lse_off]);
   m = wave_max(m);
 
-  const int64_t row = pair * D + lane * EPL;  // (t * H + h) * D
   if (m == kNegInf) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) Elem<OT>::st(out, row + e, 0.0f);
@@ -65,33 +81,53 @@ __global__ __launch_bounds__(256) void merge_kernel(void* __restrict__ out,
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
   float wsum = 0.0f;
-  const int64_t part_stride = T * H * D;
-  // parts in batches of 8: the loads of a batch are independent and go out
-  // together (one memory latency per batch, not per part)
-  int p = 0;
-  for (; p + 8 <= S; p += 8) {
-    float w[8], x[8][EPL];
+  // weight of part p (p wave-uniform): with at most 64 parts every LSE is
+  // in a lane already; the choice is made once, outside the loops, so each
+  // batch's row loads stay together
+  auto accumulate = [&](auto lse_in_lanes) {
+    constexpr bool IN_LANES = decltype(lse_in_lanes)::value;
+    auto weight = [&](int p) {
+      const float l = IN_LANES ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse_l), p))
+                               : parts_lse[p * lse_stride + lse_off];
+      return fast_exp2((l - m) * kLog2e);
+    };
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      w[j] = fast_exp2((parts_lse[(p + j) * lse_stride + lse_off] - m) * kLog2e);
+    for (int j = 0; j < NB; ++j)
+      if (j < nb0) {
+        const float w = weight(j);
+        wsum += w;
+        // an empty part (w = 0) may hold anything, finite or not
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[j][e] = Elem<PT>::ld(parts, (p + j) * part_stride + row + e);
+        for (int e = 0; e < EPL; ++e) acc[e] += w != 0.0f ? w * x0[j][e] : 0.0f;
+      }
+    // the other parts in batches of 8: the loads of a batch are independent
+    // and go out together
+    int p = nb0;
+    for (; p + 8 <= S; p += 8) {
+      float w[8], x[8][EPL];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        w[j] = weight(p + j);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[j][e] = Elem<PT>::ld(parts, (p + j) * part_stride + row + e);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        wsum += w[j];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += w[j] != 0.0f ? w[j] * x[j][e] : 0.0f;
+      }
     }
+    for (; p < S; ++p) {
+      const float w = weight(p);
+      wsum += w;
+      if (w == 0.0f) continue;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      wsum += w[j];
-      // an empty part (w = 0) may hold anything, finite or not
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += w[j] != 0.0f ? w[j] * x[j][e] : 0.0f;
+      for (int e = 0; e < EPL; ++e) acc[e] += w * Elem<PT>::ld(parts, p * part_stride + row + e);
     }
-  }
-  for (; p < S; ++p) {
-    const float w = fast_exp2((parts_lse[p * lse_stride + lse_off] - m) * kLog2e);
-    wsum += w;
-    if (w == 0.0f) continue;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w * Elem<PT>::ld(parts, p * part_stride + row + e);
-  }
+  };
+  if (S <= 64) accumulate(std::true_type{});
+  else accumulate(std::false_type{});
   const float inv = 1.0f / wsum;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) Elem<OT>::st(out, row + e, acc[e] * inv);
