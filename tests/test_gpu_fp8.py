@@ -80,6 +80,7 @@ DECODE = [
      False, 3),
     ("g1_d256_alibi", [33, 260, 1], 4, 4, 256, 16, torch.bfloat16, -1, 0.0, True, False, 2),
     ("g16_d128_hpw1", [100, 2049], 16, 1, 128, 64, torch.bfloat16, -1, 0.0, False, False, 1),
+    ("g2_d128_alibi_hpw2", [33, 500, 2], 8, 4, 128, 16, torch.bfloat16, -1, 0.0, True, False, 2),
 ]
 
 
