@@ -212,36 +212,38 @@ def spin_up(fn, seconds: float = WARM_SECONDS):
 def run_prefill(args, pa, runner):
     w = W.prefill_batch()
     call = w.steps[0].calls[0]
-    cache = runner.PagedCache(w)
+    cache = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
     cache.sinks = bench_sinks(args, w)
     k, v, s = cache.step_inputs(w.steps[0])
     cb = cache.call_buffers(call)
     pre_t, rac_t = Timed(), Timed()
     for _ in range(args.warmup):
-        pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+        cache.write(k, v, s)
         cache.run(cb)
-    spin_up(lambda: (pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s),
-                     cache.run(cb)))
+    spin_up(lambda: (cache.write(k, v, s), cache.run(cb)))
     queue_ahead(args.steps)
     for _ in range(args.steps):
         with rac_t:
-            pa.reshape_and_cache(k, v, cache.key_cache, cache.value_cache, s)
+            cache.write(k, v, s)
         with pre_t:
             cache.run(cb)
     torch.cuda.synchronize()
     flops = prefill_flops(w, call)
     ms = pre_t.mean_ms()
     tflops = flops / (ms * 1e-3) / 1e12
-    rac_bytes = 2 * int(s.numel()) * w.num_kv_heads * w.head_size * 2 * 2
+    # rows read (16-bit) and written (cache element)
+    rac_bytes = 2 * int(s.numel()) * w.num_kv_heads * w.head_size * (2 + (1 if args.kv_fp8 else 2))
     digest = source_digest("prefill.hip", "common.h")
     return {
-        "value": round(tflops, 2), "unit": "TFLOP/s", "workload": w.name,
+        "value": round(tflops, 2), "unit": "TFLOP/s",
+        "workload": w.name + ("_kvfp8" if args.kv_fp8 else ""),
         "ms_per_call": round(ms, 4), "flops": flops, "query_tokens": int(call.q.shape[0]),
         "reshape_and_cache": {"ms": round(rac_t.mean_ms(), 4),
                               "GB/s": round(rac_bytes / (rac_t.mean_ms() * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile("prefill", digest)},
+                     "traffic": traffic_from_profile(
+                         "prefill" + ("_kvfp8" if args.kv_fp8 else ""), digest)},
     }
 
 

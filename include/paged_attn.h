@@ -125,8 +125,11 @@ int reshape_and_cache(const void* key, const void* value,
  *   Query head h reads KV head h / (num_heads / num_kv_heads).
  *   A query that sees no key gets out = 0 and lse = -inf (lse = sink_h
  *   with sinks).
- *   kv_cache_dtype  must equal dtype here: an fp8 cache gives
- *                   PA_ERR_UNSUPPORTED (it is read by paged_attn_decode).
+ *   kv_cache_dtype, k_scale, v_scale: a 16-bit cache (= dtype) or an fp8
+ *                   cache with its scales (see the conventions above); the
+ *                   K scale multiplies every score and the V scale the
+ *                   result, and the products run on the 16-bit values of
+ *                   the codes (exact), as for a 16-bit cache.
  *   PA_ERR_UNSUPPORTED also for num_seqs > 65535, more than 128 query heads
  *   per KV head, max_seqlen_k >= 2^24 or num_kv_heads * max_seqlen_q >=
  *   2^31 (grid limits).
@@ -222,7 +225,7 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
  * with causal = 1 on the same batch; the shared prefix is read once for the
  * batch rather than once per sequence.
  *
- *   Arguments as for paged_attn_prefill (16-bit cache only; causal, no
+ *   Arguments as for paged_attn_prefill (16-bit or fp8 cache; causal, no
  *   window, no ALiBi: the page's cascade supports neither), plus
  *   sinks              nullable, as for prefill; folded into the prefix
  *                      part only (the page adds s_aux to the prefix LSE);

@@ -154,7 +154,7 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
                              num_blocks, scale, window_left, softcap, dtype, q, key_cache,
                              value_cache, seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
-  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, false);
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -196,6 +196,9 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
   p.sinks = sinks;
   p.num_splits = 1;
   p.dtype = static_cast<pa::Dtype>(dtype);
+  p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   return hip_result(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -298,7 +301,7 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
                              num_blocks, scale, -1, softcap, dtype, q, key_cache, value_cache,
                              seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
-  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, false);
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -352,6 +355,9 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
   p.sinks = sinks;
   p.num_splits = 1;
   p.dtype = static_cast<pa::Dtype>(dtype);
+  p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   return hip_result(pa::launch_cascade(p, common_prefix_len, max_prefix_splits, parts_out,
                                        parts_lse, work_ints, static_cast<hipStream_t>(stream)),
                     fn);

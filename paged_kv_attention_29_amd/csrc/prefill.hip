@@ -46,7 +46,7 @@ namespace {
 constexpr int kKT = 64;       // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-enum { kSoftcap = 1, kAlibi = 2 };
+enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4 };
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -76,6 +76,10 @@ struct PrefillArgs {
   // attention sinks [Hq] (fp32, nullable): one more logit per head in the
   // softmax denominator, without a value; folded into split 0 only
   const float* sinks;
+  // fp8 (e4m3) cache: device fp32 scales (a stored code times the scale is
+  // the K / V value); null for a 16-bit cache
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
@@ -91,8 +95,14 @@ template <int D>
 constexpr int kRows = 32 * kNW<D>;     // MFMA rows per workgroup
 template <int D>
 constexpr int kTileBytes = kKT * D * 2;  // one of K or V
-template <int D>
-constexpr size_t prefill_lds_bytes() { return (size_t)kNST<D> * 2 * kTileBytes<D>; }
+// An fp8 cache lands in the ring as codes (half the bytes per stage) and
+// each tile is widened into one 16-bit K/V tile pair after the ring, which
+// the MFMA operand reads use exactly as they use a 16-bit stage.
+template <int D, bool F8>
+constexpr size_t prefill_lds_bytes() {
+  return F8 ? (size_t)kNST<D> * 2 * (kTileBytes<D> / 2) + 2 * kTileBytes<D>
+            : (size_t)kNST<D> * 2 * kTileBytes<D>;
+}
 
 // LDS has 64 banks of 4 bytes: a ds_read_b128 serves 16 lanes per cycle and
 // a ds_read_b64_tr_b16 32 lanes, and each such group must cover all 64
@@ -181,15 +191,18 @@ template <typename T, int D, int FEAT>
 __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(PrefillArgs a) {
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
+  constexpr bool F8 = FEAT & kFp8;
   constexpr int NW = kNW<D>;
   constexpr int NST = kNST<D>;
   constexpr int TB = kTileBytes<D>;
   constexpr int KQ = D / 16;           // QK mfma steps along D
   constexpr int DC = D / 32;           // PV output chunks of 32 head dims
-  constexpr int RB = 2 * D;            // bytes per key row
+  constexpr int RB = 2 * D;            // bytes per key row of a 16-bit tile
+  constexpr int RBC = F8 ? D : RB;     // bytes per key row as cached (and staged)
+  constexpr int TBC = kKT * RBC;       // one of K or V as staged
   constexpr int RW = kKT / NW;         // key rows fetched per wave per tile
-  constexpr int NI = RW * RB / 1024;   // DMA instructions per wave per tile, each of K and V
-  constexpr int ROWS_PER_I = 1024 / RB;
+  constexpr int NI = RW * RBC / 1024;  // DMA instructions per wave per tile, each of K and V
+  constexpr int ROWS_PER_I = 1024 / RBC;
   static_assert(NI >= 1 && RW <= 16, "tile split");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -198,6 +211,14 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31;
   const int g2 = lane >> 5;
+  float v_scale = 1.0f;
+  if constexpr (F8) {
+    // the K scale multiplies every score, the V scale the result
+    const float ks = *a.k_scale;
+    a.scale_log2 *= ks;
+    a.scale_over_cap *= ks;
+    v_scale = *a.v_scale;
+  }
 
   // Grid (Hkv * query tiles, sequences), x = tile' * Hkv + g.  Workgroups are
   // dispatched to the 8 XCDs round-robin in linear order, so with 8 KV heads
@@ -275,22 +296,27 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   wait_vmcnt<KQ>();  // the block ids (issued before Q) landed
   claim(ids);
 
-  const uint16_t* kc = a.kc + (int64_t)g * D;
-  const uint16_t* vc = a.vc + (int64_t)g * D;
+  const char* kc = reinterpret_cast<const char*>(a.kc) + (int64_t)g * RBC;
+  const char* vc = reinterpret_cast<const char*>(a.vc) + (int64_t)g * RBC;
 
   // ---- DMA addressing.  Lane l of instruction i of this wave writes LDS
   //      bytes wave*RW*RB + i*1024 + 16*l of the tile: key row
   //      wave*RW + i*ROWS_PER_I + l/(RB/16), slot l % (RB/16).
-  const uint32_t row_bytes = static_cast<uint32_t>(a.Hkv) * D * 2;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.Hkv) * RBC;
   const uint32_t smem0 = lds_addr(smem);
-  // the piece that belongs at this lane's slot of instruction i's row
-  auto dma_row = [&](int i) { return wave * RW + i * ROWS_PER_I + lane / (RB / 16); };
-  auto dma_kp = [&](int i) { return ((lane % (RB / 16)) ^ swz_k<D>(dma_row(i))) * 16; };
-  auto dma_vp = [&](int i) { return ((lane % (RB / 16)) ^ swz_v<D>(dma_row(i))) * 16; };
+  // the piece that belongs at this lane's slot of instruction i's row (an
+  // fp8 stage is stored unpermuted: the widening pass applies the swizzle)
+  auto dma_row = [&](int i) { return wave * RW + i * ROWS_PER_I + lane / (RBC / 16); };
+  auto dma_kp = [&](int i) {
+    return F8 ? (lane % (RBC / 16)) * 16 : ((lane % (RB / 16)) ^ swz_k<D>(dma_row(i))) * 16;
+  };
+  auto dma_vp = [&](int i) {
+    return F8 ? (lane % (RBC / 16)) * 16 : ((lane % (RB / 16)) ^ swz_v<D>(dma_row(i))) * 16;
+  };
   uint32_t dma_k[NI], dma_v[NI];  // byte offset from the wave's first row (all rows present)
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint32_t rr = i * ROWS_PER_I + lane / (RB / 16);
+    const uint32_t rr = i * ROWS_PER_I + lane / (RBC / 16);
     dma_k[i] = rr * row_bytes + dma_kp(i);
     dma_v[i] = rr * row_bytes + dma_vp(i);
   }
@@ -301,10 +327,10 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     const int gk = group_key(tile);
     const int gq = div_magic(gk, a.bs_magic);
     const int64_t slot0 = (int64_t)blk * a.bs + (gk - gq * a.bs);  // cache slot of key gk
-    const char* kb = reinterpret_cast<const char*>(kc) + slot0 * row_bytes;
-    const char* vb = reinterpret_cast<const char*>(vc) + slot0 * row_bytes;
-    const uint32_t kst = smem0 + stage * 2 * TB + wave * RW * RB;
-    const uint32_t vst = kst + TB;
+    const char* kb = kc + slot0 * row_bytes;
+    const char* vb = vc + slot0 * row_bytes;
+    const uint32_t kst = smem0 + stage * 2 * TBC + wave * RW * RBC;
+    const uint32_t vst = kst + TBC;
     if (kbase + wave * RW + RW <= L) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -501,6 +527,35 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     }
   };
 
+  // ---- fp8 cache: widen this wave's RW rows of the staged K and V tiles
+  //      (codes, unpermuted) into the 16-bit tile pair after the ring, with
+  //      the operand swizzles, then a barrier.  Every wave widens its rows of
+  //      every tile, also of tiles it skips itself.
+  auto widen = [&](int stage) {
+    const char* k8 = smem + stage * 2 * TBC;
+    const char* v8 = k8 + TBC;
+    char* k16 = smem + NST * 2 * TBC;
+    char* v16 = k16 + TB;
+    constexpr int PPR = D / 8;           // 8-element pieces per row
+    constexpr int PPL = RW * PPR / 64;   // pieces per lane
+    static_assert(PPL * 64 == RW * PPR, "widening split");
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int q = lane + 64 * i;
+      const int r = wave * RW + q / PPR;
+      const int c = q % PPR;
+      const u32x2 kw = *reinterpret_cast<const u32x2*>(k8 + r * RBC + 8 * c);
+      const u32x2 vw = *reinterpret_cast<const u32x2*>(v8 + r * RBC + 8 * c);
+      const v4s k0 = T::from_fp8x4(kw[0]), k1 = T::from_fp8x4(kw[1]);
+      const v4s v0 = T::from_fp8x4(vw[0]), v1 = T::from_fp8x4(vw[1]);
+      *reinterpret_cast<v8s*>(k16 + r * RB + 16 * (c ^ swz_k<D>(r))) =
+          v8s{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      *reinterpret_cast<v8s*>(v16 + r * RB + 16 * (c ^ swz_v<D>(r))) =
+          v8s{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+    lds_barrier();
+  };
+
   // ---- prologue: the first NST - 1 tiles
   // (t_begin < t_end whenever the tile has a query row: its own key is visible)
   const int n = t_end - t_begin;
@@ -539,7 +594,11 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       issue_tile(tile + NST - 1, id_of(jt), pst);
     }
     const bool act = tile_active(kbase);
-    const uint32_t kst = smem0 + st * 2 * TB;
+    uint32_t kst = smem0 + st * 2 * TB;
+    if constexpr (F8) {
+      widen(st);
+      kst = smem0 + NST * 2 * TBC;
+    }
     v16f sacc[2];
     v8s pb[4];
     if (act) mfma_block(std::false_type{}, std::true_type{}, 0u, kst, pb, sacc);
@@ -568,7 +627,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       m_fin = M;
     }
   }
-  const float inv = l_tot > 0.f ? o_scale * __builtin_amdgcn_rcpf(l_tot) : 0.0f;
+  const float inv = l_tot > 0.f ? o_scale * v_scale * __builtin_amdgcn_rcpf(l_tot) : 0.0f;
   const int64_t qrow = q0 + tok0 + tk;
   const int64_t part = blockIdx.z;  // key split (0 without splits)
   uint16_t* orow = a.out + ((part * a.total_q + qrow) * a.Hq + head) * D + 4 * g2;
@@ -592,7 +651,8 @@ int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream
   if (!attr_set) {
     attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D, FEAT>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   static_cast<int>(prefill_lds_bytes<D>())) == hipSuccess;
+                                   static_cast<int>(prefill_lds_bytes<D, (FEAT & kFp8) != 0>())) ==
+               hipSuccess;
   }
   PrefillArgs a = args;
   a.tok_per_tile = kRows<D> / a.G;
@@ -602,25 +662,25 @@ int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream
   const int splits = a.key_split > 0 ? n_ksplits : 1;
   const dim3 grid(static_cast<unsigned>(a.Hkv * a.n_qtiles), a.B, static_cast<unsigned>(splits));
   hipLaunchKernelGGL((prefill_kernel<T, D, FEAT>), grid, dim3(kNW<D> * 64),
-                     prefill_lds_bytes<D>(), stream, a);
+                     (prefill_lds_bytes<D, (FEAT & kFp8) != 0>()), stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <typename T, int D>
+template <typename T, int D, int F8>
 int launch_feat(const PrefillArgs& a, int mq, int ns, bool softcap, bool alibi, hipStream_t s) {
-  if (softcap && alibi) return launch_p<T, D, kSoftcap | kAlibi>(a, mq, ns, s);
-  if (softcap) return launch_p<T, D, kSoftcap>(a, mq, ns, s);
-  if (alibi) return launch_p<T, D, kAlibi>(a, mq, ns, s);
-  return launch_p<T, D, 0>(a, mq, ns, s);
+  if (softcap && alibi) return launch_p<T, D, F8 | kSoftcap | kAlibi>(a, mq, ns, s);
+  if (softcap) return launch_p<T, D, F8 | kSoftcap>(a, mq, ns, s);
+  if (alibi) return launch_p<T, D, F8 | kAlibi>(a, mq, ns, s);
+  return launch_p<T, D, F8>(a, mq, ns, s);
 }
 
-template <typename T>
+template <typename T, int F8>
 int launch_t(const PrefillArgs& a, int D, int mq, int ns, bool softcap, bool alibi,
              hipStream_t s) {
   switch (D) {
-    case 64: return launch_feat<T, 64>(a, mq, ns, softcap, alibi, s);
-    case 128: return launch_feat<T, 128>(a, mq, ns, softcap, alibi, s);
-    default: return launch_feat<T, 256>(a, mq, ns, softcap, alibi, s);
+    case 64: return launch_feat<T, 64, F8>(a, mq, ns, softcap, alibi, s);
+    case 128: return launch_feat<T, 128, F8>(a, mq, ns, softcap, alibi, s);
+    default: return launch_feat<T, 256, F8>(a, mq, ns, softcap, alibi, s);
   }
 }
 
@@ -655,11 +715,18 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.alibi = p.alibi_slopes;
   a.key_split = p.key_split;
   a.sinks = p.sinks;
+  a.k_scale = p.k_scale;
+  a.v_scale = p.v_scale;
   const int ns = p.key_split > 0 ? (p.max_seqlen_k + p.key_split - 1) / p.key_split : 1;
   const bool alibi = p.alibi_slopes != nullptr;
+  if (p.kv_fp8) {
+    if (p.dtype == kBF16)
+      return launch_t<BF16, kFp8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+    return launch_t<F16, kFp8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+  }
   if (p.dtype == kBF16)
-    return launch_t<BF16>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
-  return launch_t<F16>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+    return launch_t<BF16, 0>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+  return launch_t<F16, 0>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
 }
 
 }  // namespace pa

@@ -84,8 +84,10 @@ def test_fp8_cache_validation(lib):
     assert _decode(lib, kvdt=F8, ks=1, vs=None) == -1
     assert _decode(lib, kvdt=lib.PA_BF16) == -2                 # cache type must match q
     assert _decode(lib, kvdt=9, ks=1, vs=1) == -2
-    assert _prefill(lib, kvdt=F8, ks=1, vs=1) == -2             # prefill reads 16-bit caches
-    assert _cascade(lib, kvdt=F8, ks=1, vs=1) == -2
+    # prefill and the cascade read fp8 caches too, with the same rules
+    assert _prefill(lib, kvdt=F8, ks=None, vs=1) == -1
+    assert _prefill(lib, kvdt=9, ks=1, vs=1) == -2
+    assert _cascade(lib, kvdt=F8, ks=1, vs=None) == -1
     assert lib.pa_last_error().startswith("paged_attn_cascade")
 
 

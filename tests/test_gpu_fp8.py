@@ -1,8 +1,9 @@
 """GPU parity of the fp8 (e4m3) KV cache: reshape_and_cache quantising into
 fp8 codes (bit-exact against the oracle's quantiser, including saturation,
 infinities, negative zero, padding slots and unaligned strides) and
-paged_attn_decode reading an fp8 cache (against the oracle attending the
-dequantised cache in float64: max-abs 2e-2 / mean-abs 2e-3, LSE 1e-2)."""
+paged_attn_decode, paged_attn_prefill and paged_attn_cascade reading an fp8
+cache (against the oracle attending the dequantised cache in float64:
+max-abs 2e-2 / mean-abs 2e-3, LSE 1e-2)."""
 import pytest
 import torch
 
@@ -164,3 +165,88 @@ def test_fp8_end_to_end_write_then_decode(pa):
                            table, D ** -0.5)
     assert_attn_close(out, ro, "fp8 end to end")
     assert_lse_close(lse, rl, "fp8 end to end lse")
+
+
+PREFILL = [
+    # name, context, q_lens, Hq, Hkv, D, bs, dtype, causal, window_left, softcap, alibi, sinks
+    ("g4_d128_causal", [0, 100, 37, 1000], [200, 1, 64, 77], 32, 8, 128, 16, torch.bfloat16,
+     True, -1, 0.0, False, False),
+    ("g8_d64_fp16_window_cap_sinks", [5, 300], [70, 129], 16, 2, 64, 32, torch.float16, True,
+     50, 3.0, False, True),
+    ("g1_d256_alibi", [33, 0], [40, 90], 4, 4, 256, 16, torch.bfloat16, True, -1, 0.0, True,
+     False),
+    ("g16_d128_noncausal", [20, 3], [33, 10], 16, 1, 128, 64, torch.bfloat16, False, -1, 0.0,
+     False, False),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
+def test_prefill_fp8_cache(pa, case):
+    """paged_attn_prefill over an fp8 cache against the oracle attending the
+    dequantised cache (ragged chunks after cached context, partial tiles)."""
+    name, ctx, q_lens, Hq, Hkv, D, bs, dtype, causal, wl, cap, alibi, sinks = case
+    print(f"\n[gpu-case] prefill fp8 {name}", flush=True)
+    seed = len(name) * 5
+    k_scale, v_scale = 0.011, 0.0075
+    lens = [c + n for c, n in zip(ctx, q_lens)]
+    kc, vc, table = _fp8_cache(seed, lens, Hkv, D, bs, k_scale, v_scale)
+    g = torch.Generator().manual_seed(seed + 1)
+    cu = [0]
+    for n in q_lens:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    q = (torch.randn(T, Hq, D, generator=g) * 0.5).to(dtype)
+    slopes = torch.rand(Hq, generator=g) * 0.05 if alibi else None
+    sk = torch.randn(Hq, generator=g) if sinks else None
+    scale = D ** -0.5
+    dev = lambda t: None if t is None else t.cuda()
+    out = torch.full((T, Hq, D), float("nan"), dtype=dtype, device="cuda")
+    lse = torch.full((Hq, T), float("nan"), device="cuda")
+    pa.paged_attn_prefill(out, q.cuda(), kc.cuda(), vc.cuda(),
+                          torch.tensor(cu, dtype=torch.int32, device="cuda"),
+                          torch.tensor(lens, dtype=torch.int32, device="cuda"), table.cuda(),
+                          max(q_lens), max(lens), scale, causal, wl, cap, dev(slopes), lse=lse,
+                          sinks=dev(sk), k_scale=torch.tensor([k_scale], device="cuda"),
+                          v_scale=torch.tensor([v_scale], device="cuda"))
+    torch.cuda.synchronize()
+    kf, vf = e4m3_dequantize(kc, k_scale), e4m3_dequantize(vc, v_scale)
+    kf[torch.isnan(kf)] = 0.0                  # (the spare block is never visible)
+    vf[torch.isnan(vf)] = 0.0
+    ro, rl = oracle.attend(q, kf, vf, cu, lens, table, scale, causal, wl, cap, slopes, sinks=sk)
+    assert_attn_close(out, ro, name)
+    assert_lse_close(lse, rl, f"{name} lse")
+
+
+def test_cascade_fp8_cache(pa):
+    """paged_attn_cascade over an fp8 cache (decode-like batch and longer
+    chunks) against the oracle's cascade on the dequantised cache, and the
+    fp8 plain causal prefill of the same batch."""
+    from test_gpu_cascade import _case
+    print("\n[gpu-case] cascade fp8", flush=True)
+    prefix, q_lens, extra = 256, [1, 37, 64, 1, 129], [0, 100, 7, 300, 64]
+    Hq, Hkv, D, bs = 32, 8, 128, 16
+    q, kc, vc, cu, lens, table = _case(41, prefix, q_lens, extra, Hq, Hkv, D, bs, torch.bfloat16)
+    k_scale, v_scale = 0.011, 0.0075
+    kc8, vc8 = e4m3_quantize(kc, k_scale), e4m3_quantize(vc, v_scale)   # NaN blocks: 0x7F
+    scale = D ** -0.5
+    T = cu[-1]
+    ks = torch.tensor([k_scale], device="cuda")
+    vs = torch.tensor([v_scale], device="cuda")
+    cud = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    lensd = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qd, kd, vd, td = q.cuda(), kc8.cuda(), vc8.cuda(), table.cuda()
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Hq, T), float("nan"), device="cuda")
+    pa.paged_attn_cascade(out, qd, kd, vd, cud, lensd, td, max(q_lens), max(lens), scale, prefix,
+                          lse=lse, k_scale=ks, v_scale=vs)
+    out_p = torch.empty_like(out)
+    pa.paged_attn_prefill(out_p, qd, kd, vd, cud, lensd, td, max(q_lens), max(lens), scale, True,
+                          k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    kf, vf = e4m3_dequantize(kc8, k_scale), e4m3_dequantize(vc8, v_scale)
+    kf[torch.isnan(kf)] = 0.0
+    vf[torch.isnan(vf)] = 0.0
+    ro, rl = oracle.cascade(q, kf, vf, cu, lens, table, scale, prefix)
+    assert_attn_close(out, ro, "cascade fp8")
+    assert_lse_close(lse, rl, "cascade fp8 lse")
+    assert_attn_close(out_p, ro, "prefill fp8")
