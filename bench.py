@@ -168,9 +168,7 @@ def run_decode(args, pa, runner, w):
         step(i, False)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    # the same steps again with HIP events around each kernel, queued behind
-    # a GPU spin so the events time GPU execution, not host launch gaps
-    queue_ahead(args.steps)
+    # the same steps again with HIP events around each kernel
     for i in range(args.steps):
         step(i, True)
     torch.cuda.synchronize()
@@ -186,16 +184,6 @@ def bench_sinks(args, w):
         return None
     g = torch.Generator().manual_seed(77)
     return (torch.randn(w.num_heads, generator=g) * 2.0).to("cuda")
-
-
-def queue_ahead(steps: int):
-    """Keep the GPU busy (a bounded spin kernel, about 0.5 ms per step at the
-    2.4 GHz shader clock, longer than the host takes to enqueue a step) while
-    the host enqueues the next timed launches, so the events around each
-    launch see the launches back to back on the GPU rather than the host's
-    launch latency."""
-    torch.cuda.synchronize()
-    torch.cuda._sleep(1_200_000 * max(1, steps))
 
 
 def spin_up(fn, seconds: float = WARM_SECONDS):
@@ -221,7 +209,6 @@ def run_prefill(args, pa, runner):
         cache.write(k, v, s)
         cache.run(cb)
     spin_up(lambda: (cache.write(k, v, s), cache.run(cb)))
-    queue_ahead(args.steps)
     for _ in range(args.steps):
         with rac_t:
             cache.write(k, v, s)
