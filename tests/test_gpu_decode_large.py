@@ -172,3 +172,36 @@ def test_decode_many_short_sequences(pa, runner):
     po, pl = oracle.decode_splits(call.q, kc, vc, call.seq_lens.tolist(), bt, w.scale, S)
     assert_attn_close(cb.part_out, po, "parts")
     assert_lse_close(cb.part_lse, pl, "part lse")
+
+
+@pytest.mark.timeout(300)
+def test_decode_ranked_order_at_its_limits(pa, runner):
+    """1024 sequences and 64 splits, the largest batch the in-kernel work-item
+    ranking takes (16 chunks of 64 sequences, the difference counter past the
+    64th split), with one-key sequences and mostly empty splits.  The 64 parts
+    merged on the GPU must equal the oracle's unsplit decode (a misplaced or
+    skipped item changes the merge), and exactly the splits the oracle's
+    bounds leave empty must carry lse = -inf."""
+    B, S = 1024, 64
+    _announce(f"decode ranked order at its limits: B={B} S={S}")
+    rng = np.random.default_rng(8)
+    ctx = rng.integers(0, 300, size=B)
+    ctx[::5] = 0
+    w = W.custom("ranklim", 34, ctx, [1] * B, 8, 2, 64, 16, torch.bfloat16, "decode",
+                 num_splits=S)
+    cache, call, cb = _setup(runner, pa, w, S)
+    _poison(cb)
+    mx = int(call.seq_lens.max())
+    _decode(pa, w, cache, cb, cb.seq_lens, mx)
+    pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
+    torch.cuda.synchronize()
+    lens = call.seq_lens.tolist()
+    kc, vc = oracle_cache(w, 0)
+    bt = torch.from_numpy(w.block_table[np.asarray(call.seq_ids)])
+    ro, rl = oracle.decode(call.q, kc, vc, lens, bt, w.scale)
+    assert_attn_close(cb.out, ro, "merged parts")
+    assert_lse_close(cb.lse, rl, "merged lse")
+    empty = torch.tensor([[lo >= hi for (lo, hi) in oracle.split_bounds(L, S, w.block_size, mx)]
+                          for L in lens]).T                      # [S, B]
+    plse = cb.part_lse.cpu()                                     # [S, Hq, B]
+    assert torch.equal(torch.isneginf(plse), empty[:, None, :].expand_as(plse))
