@@ -150,10 +150,6 @@ constexpr int kRankMaxB = 1024;
 constexpr int kRankMaxS = 64;
 static_assert((kRankMaxS + 1 + kRankMaxB) * 4 <= kRankScratchBytes, "ranking scratch size");
 
-struct ItemRef {
-  int g0, b, split, L;
-};
-
 // wave 0 only; sh = LDS scratch, res = the hand-off slot (4 ints)
 template <int HPW>
 __device__ void ranked_item_wave0(const DecodeArgs& a, int* sh, int* res) {
