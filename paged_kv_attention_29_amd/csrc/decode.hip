@@ -72,9 +72,10 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 // Their query heads are the first G * HPW columns of the MFMA tile.
 // Keys per iteration: NT MFMA row tiles of 16, so that a wave keeps 16 KB of
 // K/V in flight while it computes the previous step (one tile for two heads
-// or D = 256).
-template <int D, int HPW>
-constexpr int kNT = (D <= 128 && HPW == 1) ? 2 : 1;
+// or D = 256; an fp8 cache at D = 256, whose rows are half as long and
+// whose workgroup has the CU to itself, takes two).
+template <int D, int HPW, bool F8 = false>
+constexpr int kNT = ((D <= 128 && HPW == 1) || (F8 && D == 256)) ? 2 : 1;
 
 // LDS: per-wave V slabs of 16 * NT rows (pitch D + 16 elements: the 32-byte
 // pad spreads the 16 rows a transpose read touches over all banks) and the
@@ -82,9 +83,9 @@ constexpr int kNT = (D <= 128 && HPW == 1) ? 2 : 1;
 // (fp32).
 template <int D, int HPW>
 constexpr int kVPitch = HPW * D + 16;
-template <int D, int HPW>
+template <int D, int HPW, bool F8>
 constexpr size_t vslab_bytes() {
-  return (size_t)kWaves * 16 * kNT<D, HPW> * kVPitch<D, HPW> * 2;
+  return (size_t)kWaves * 16 * kNT<D, HPW, F8> * kVPitch<D, HPW> * 2;
 }
 template <int D, int HPW>
 constexpr size_t comb_bytes(int G) {
@@ -95,16 +96,16 @@ constexpr size_t comb_bytes(int G) {
 // hands its result over in a 16-byte slot past the slabs, the combine area
 // and the scratch, which nothing else writes.
 constexpr size_t kRankScratchBytes = (64 + 1 + 1024) * 4;
-template <int D, int HPW>
+template <int D, int HPW, bool F8>
 constexpr size_t rank_slot_offset(int G) {
-  const size_t vc = vslab_bytes<D, HPW>() > comb_bytes<D, HPW>(G) ? vslab_bytes<D, HPW>()
-                                                                   : comb_bytes<D, HPW>(G);
+  const size_t vc = vslab_bytes<D, HPW, F8>() > comb_bytes<D, HPW>(G) ? vslab_bytes<D, HPW, F8>()
+                                                                       : comb_bytes<D, HPW>(G);
   const size_t m = vc > kRankScratchBytes ? vc : kRankScratchBytes;
   return (m + 15) / 16 * 16;
 }
-template <int D, int HPW>
+template <int D, int HPW, bool F8>
 constexpr size_t decode_lds_bytes(int G) {
-  return rank_slot_offset<D, HPW>(G) + 16;
+  return rank_slot_offset<D, HPW, F8>(G) + 16;
 }
 
 template <int D>
@@ -240,7 +241,7 @@ struct Dec {
   static constexpr int KK = D / 32;   // QK mfma steps along D
   static constexpr int NU = D / 64;   // fp8: 16-byte pieces of a row per lane
   static constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
-  static constexpr int NT = kNT<D, HPW>;
+  static constexpr int NT = kNT<D, HPW, F8>;
   static constexpr int KPS = 16 * NT; // keys per step
   static constexpr int P = kVPitch<D, HPW>;
   static constexpr int CP = D + 4;    // combine row: m, l, 2 pad, O[D] (16-byte aligned)
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
 
   int g0, b, split, L;
   if (a.B <= kRankMaxB && a.S <= kRankMaxS) {
-    int* res = reinterpret_cast<int*>(smem + rank_slot_offset<D, HPW>(a.G));
+    int* res = reinterpret_cast<int*>(smem + rank_slot_offset<D, HPW, K::F8>(a.G));
     if (wave == 0) ranked_item_wave0<HPW>(a, reinterpret_cast<int*>(smem), res);
     __syncthreads();
     g0 = __builtin_amdgcn_readfirstlane(res[0]);
@@ -682,9 +683,20 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
 
 template <typename T, int D, int FEAT, int HPW>
 int launch_h(const DecodeArgs& args, hipStream_t stream) {
+  constexpr bool F8 = (FEAT & kFp8) != 0;
   const int64_t items = (int64_t)(args.Hkv / HPW) * args.B * args.S;
+  const size_t lds = decode_lds_bytes<D, HPW, F8>(args.G);
+  if (lds > 65536) {
+    // (the fp8 D = 256 variants with two tiles per step use more than 64 KB)
+    static bool attr_set = false;
+    if (!attr_set) {
+      attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, FEAT, HPW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(decode_lds_bytes<D, HPW, F8>(16))) == hipSuccess;
+    }
+  }
   hipLaunchKernelGGL((decode_kernel<T, D, FEAT, HPW>), dim3(static_cast<unsigned>(items)),
-                     dim3(kWaves * 64), (decode_lds_bytes<D, HPW>(args.G)), stream, args);
+                     dim3(kWaves * 64), lds, stream, args);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
