@@ -82,6 +82,11 @@ DECODE = [
     ("g1_d256_alibi", [33, 260, 1], 4, 4, 256, 16, torch.bfloat16, -1, 0.0, True, False, 2),
     ("g16_d128_hpw1", [100, 2049], 16, 1, 128, 64, torch.bfloat16, -1, 0.0, False, False, 1),
     ("g2_d128_alibi_hpw2", [33, 500, 2], 8, 4, 128, 16, torch.bfloat16, -1, 0.0, True, False, 2),
+    # D = 256 takes two 16-key tiles per step over an fp8 cache
+    ("g2_d256_window_cap_sinks", [700, 40, 1300, 17], 8, 4, 256, 16, torch.bfloat16, 100, 5.0,
+     False, True, 4),
+    ("g8_d256_fp16_unsplit", [1, 999, 260], 16, 2, 256, 32, torch.float16, -1, 0.0, False, False,
+     1),
 ]
 
 
