@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -39,6 +40,10 @@ WARM_SECONDS = 0.3  # untimed warm-up after --warmup steps, before each timed re
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
+# written between timed repetitions (outside the timed region) so that no
+# repetition finds the previous one's data in the 256 MB Infinity Cache or
+# the 8 x 4 MB L2
+SCRATCH_MIB = 512
 CSRC = os.path.join(ROOT, "paged_kv_attention_29_amd", "csrc")
 
 
@@ -92,7 +97,8 @@ def traffic_from_profile(kernel_key: str, digest: str):
 
 
 class Timed:
-    """HIP events around each launch of one kernel on the current stream."""
+    """HIP events around each launch of one kernel on the current stream
+    (the stream the library's calls are enqueued on)."""
 
     def __init__(self):
         self.pairs = []
@@ -107,8 +113,32 @@ class Timed:
         self.b.record()
         self.pairs.append((self.a, self.b))
 
-    def mean_ms(self) -> float:
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+    def times_ms(self):
+        return sorted(a.elapsed_time(b) for a, b in self.pairs)
+
+    def median_ms(self) -> float:
+        return statistics.median(self.times_ms()) if self.pairs else 0.0
+
+    def min_ms(self) -> float:
+        return min(self.times_ms()) if self.pairs else 0.0
+
+    def summary(self, work: float, unit_div: float) -> dict:
+        """median / min time and the rate of `work` at the median (work /
+        unit_div per second)."""
+        med, mn = self.median_ms(), self.min_ms()
+        return {"median_ms": round(med, 4), "min_ms": round(mn, 4), "reps": len(self.pairs),
+                "rate": round(work / (med * 1e-3) / unit_div, 2)}
+
+
+class Flush:
+    """A 512 MiB device buffer written (a fill kernel) between timed
+    repetitions, outside the timed region."""
+
+    def __init__(self):
+        self.buf = torch.empty(SCRATCH_MIB << 18, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.buf.zero_()
 
 
 def run_decode(args, pa, runner, w):
@@ -173,8 +203,8 @@ def run_decode(args, pa, runner, w):
         step(i, True)
     torch.cuda.synchronize()
     nbytes = decode_bytes(w, call, 1 if args.kv_fp8 else 2)
-    return dict(ms_per_step=wall_ms, decode_ms=dec_t.mean_ms(), rac_ms=rac_t.mean_ms(),
-                merge_ms=merge_t.mean_ms() if merge_t.pairs else 0.0, bytes=nbytes,
+    return dict(ms_per_step=wall_ms, decode_ms=dec_t.median_ms(), decode_min_ms=dec_t.min_ms(),
+                rac_ms=rac_t.median_ms(), merge_ms=merge_t.median_ms(), bytes=nbytes,
                 tokens=int(s.numel()))
 
 
@@ -197,10 +227,16 @@ def spin_up(fn, seconds: float = WARM_SECONDS):
         torch.cuda.synchronize()
 
 
-def run_prefill(args, pa, runner):
-    w = W.prefill_batch()
-    call = w.steps[0].calls[0]
+def run_prefill(args, pa, runner, flush, w=None, call_index=0, write=True):
+    """Time reshape_and_cache of the step's new tokens and the prefill call
+    (the cache is written once more before every prefill rep, so each rep
+    runs on exactly the inputs of the first), with the scratch write
+    between repetitions."""
+    w = W.prefill_batch() if w is None else w
+    call = w.steps[0].calls[call_index]
     cache = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
+    if any(int(c) > 0 for c in w.context_lens):
+        fill_cache_on_gpu(cache, seed=w.seed)
     cache.sinks = bench_sinks(args, w)
     k, v, s = cache.step_inputs(w.steps[0])
     cb = cache.call_buffers(call)
@@ -209,29 +245,154 @@ def run_prefill(args, pa, runner):
         cache.write(k, v, s)
         cache.run(cb)
     spin_up(lambda: (cache.write(k, v, s), cache.run(cb)))
-    for _ in range(args.steps):
+    for _ in range(max(args.steps, 20)):
+        flush()
         with rac_t:
             cache.write(k, v, s)
+        flush()
         with pre_t:
             cache.run(cb)
     torch.cuda.synchronize()
     flops = prefill_flops(w, call)
-    ms = pre_t.mean_ms()
+    ms = pre_t.median_ms()
     tflops = flops / (ms * 1e-3) / 1e12
     # rows read (16-bit) and written (cache element)
     rac_bytes = 2 * int(s.numel()) * w.num_kv_heads * w.head_size * (2 + (1 if args.kv_fp8 else 2))
     digest = source_digest("prefill.hip", "common.h")
-    return {
+    key = "prefill" + ("" if w.name.startswith("prefill") else ":" + w.name)
+    out = {
         "value": round(tflops, 2), "unit": "TFLOP/s",
         "workload": w.name + ("_kvfp8" if args.kv_fp8 else ""),
-        "ms_per_call": round(ms, 4), "flops": flops, "query_tokens": int(call.q.shape[0]),
-        "reshape_and_cache": {"ms": round(rac_t.mean_ms(), 4),
-                              "GB/s": round(rac_bytes / (rac_t.mean_ms() * 1e-3) / 1e9, 1)},
+        "ms_per_call": round(ms, 4), "min_ms": round(pre_t.min_ms(), 4),
+        "reps": len(pre_t.pairs), "flops": flops, "query_tokens": int(call.q.shape[0]),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile(
-                         "prefill" + ("_kvfp8" if args.kv_fp8 else ""), digest)},
+                     "traffic": traffic_from_profile(key + ("_kvfp8" if args.kv_fp8 else ""),
+                                                     digest)},
     }
+    if write:
+        out["reshape_and_cache"] = {
+            "ms": round(rac_t.median_ms(), 4), "min_ms": round(rac_t.min_ms(), 4),
+            "GB/s": round(rac_bytes / (rac_t.median_ms() * 1e-3) / 1e9, 1),
+            "bytes": rac_bytes}
+    return out
+
+
+def fill_cache_on_gpu(cache, seed: int):
+    """Fill every slot of a cache with seeded N(0,1) values drawn on the GPU
+    (timing runs only: the bytes do not have to match the host-drawn ones
+    the parity tests use, and an 8 GB cache is drawn in a moment)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    for c in (cache.key_cache, cache.value_cache):
+        for i in range(0, c.shape[0], 16384):
+            part = c[i:i + 16384]
+            if c.dtype == torch.uint8:
+                x = torch.randn(part.shape, generator=g, device="cuda", dtype=torch.float32)
+                part.copy_((x / FP8_SCALES[0]).clamp(-448, 448).to(torch.float8_e4m3fn)
+                           .view(torch.uint8))
+            else:
+                part.normal_(generator=g)
+    torch.cuda.synchronize()
+
+
+def run_decode_call(args, pa, runner, flush, w, call_index=0):
+    """Split decode + merge of one decode call with the scratch write
+    between repetitions: kernel and whole-call times (median, min)."""
+    call = w.steps[0].calls[call_index]
+    cache = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
+    fill_cache_on_gpu(cache, seed=w.seed)
+    cache.sinks = bench_sinks(args, w)
+    cb = cache.call_buffers(call)
+    S = cb.num_splits
+    dec_t, mer_t, all_t = Timed(), Timed(), Timed()
+
+    def decode():
+        pa.paged_attn_decode(None if S > 1 else cb.out, cb.q, cache.key_cache, cache.value_cache,
+                             cb.seq_lens, cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
+                             w.softcap, cache.alibi, S, part_out=cb.part_out,
+                             part_lse=cb.part_lse, lse=None if S > 1 else cb.lse,
+                             sinks=cache.sinks, k_scale=cache.k_scale, v_scale=cache.v_scale)
+
+    def merge():
+        if S > 1:
+            pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
+
+    for _ in range(args.warmup):
+        decode()
+        merge()
+    spin_up(lambda: (decode(), merge()))
+    for _ in range(max(args.steps, 20)):
+        flush()
+        with all_t:
+            with dec_t:
+                decode()
+            with mer_t:
+                merge()
+    torch.cuda.synchronize()
+    nbytes = decode_bytes(w, call, 1 if args.kv_fp8 else 2)
+    kern = nbytes / (dec_t.median_ms() * 1e-3) / 1e9
+    whole = nbytes / (all_t.median_ms() * 1e-3) / 1e9
+    digest = source_digest("decode.hip", "common.h")
+    return {
+        "workload": w.name + ("_kvfp8" if args.kv_fp8 else ""), "num_splits": S,
+        "bytes": nbytes, "decode_ms": round(dec_t.median_ms(), 4),
+        "decode_min_ms": round(dec_t.min_ms(), 4), "merge_ms": round(mer_t.median_ms(), 4),
+        "call_ms": round(all_t.median_ms(), 4), "reps": len(dec_t.pairs),
+        "call_GB/s": round(whole, 1),
+        "roofline": {"bound": "hbm", "achieved": round(kern, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(
+                         f"decode:{w.name}{'_kvfp8' if args.kv_fp8 else ''}:S{S}", digest),
+                     "kernel": "paged_attn_decode"},
+    }
+
+
+def measured_peaks(pa):
+    """Measured-achievable ceilings beside the vendor peaks: the best of a
+    small sweep of plain streaming read / copy kernels over 4 GiB
+    (pa_probe_stream), and a large bf16 GEMM through torch (hipBLASLt)."""
+    import ctypes
+    lib = pa.lib
+    lib.pa_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pa_probe_stream.restype = ctypes.c_int
+    n = 4 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(n // 8, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def best(mode, nbytes, moved):
+        res = {}
+        for wgs in (1024, 2048, 4096, 8192):
+            for unroll in (4, 8):
+                t = Timed()
+                for r in range(8):
+                    with t:
+                        rc = lib.pa_probe_stream(mode, src.data_ptr(), dst.data_ptr(), nbytes, wgs,
+                                                 unroll, stream)
+                    assert rc == 0, rc
+                torch.cuda.synchronize()
+                res[(wgs, unroll)] = moved / (t.median_ms() * 1e-3) / 1e9
+        k = max(res, key=res.get)
+        return round(res[k], 1), {"workgroups": k[0], "loads_per_lane": k[1]}
+
+    rd, rd_cfg = best(0, n, n)
+    cp, cp_cfg = best(1, n // 2, n)       # 2 GiB read + 2 GiB written
+    del src, dst
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    c = a @ b
+    t = Timed()
+    for _ in range(10):
+        with t:
+            torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    gemm = 2 * 8192 ** 3 / (t.median_ms() * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_stream_read_GB/s": rd, "read_probe": rd_cfg,
+            "hbm_copy_GB/s": cp, "copy_probe": cp_cfg,
+            "bf16_gemm_TFLOP/s": round(gemm, 1), "gemm": "8192^3 bf16 torch.matmul (hipBLASLt)"}
 
 
 def cpu_baseline(w, seconds: float = 10.0, max_passes: int = 100, sinks=None):
@@ -442,6 +603,8 @@ def main():
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default run: skip the mixed and long-context workloads and the probes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sinks", action="store_true",
                     help="decode/mixed/long: pass per-head attention-sink logits")
@@ -502,7 +665,9 @@ def main():
                    "attention_sinks": bool(args.sinks)},
         "kernels_ms": {"reshape_and_cache": round(r["rac_ms"], 4),
                        "paged_attn_decode": round(r["decode_ms"], 4),
-                       "merge_attn_states": round(r["merge_ms"], 4)},
+                       "paged_attn_decode_min": round(r["decode_min_ms"], 4),
+                       "merge_attn_states": round(r["merge_ms"], 4),
+                       "statistic": f"median over {args.steps} launches (HIP events)"},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(
@@ -510,8 +675,24 @@ def main():
                          digest),
                      "kernel": "paged_attn_decode", "bytes_per_launch": r["bytes"]},
     }
+    flush = Flush()
     if not args.no_prefill and args.workload == "decode":
-        out["prefill"] = run_prefill(args, pa, runner)
+        out["prefill"] = run_prefill(args, pa, runner, flush)
+    if not args.no_extra and args.workload == "decode":
+        # the other configured workloads, each call timed on its own
+        wm = W.mixed_batch()
+        out["mixed"] = {"decode": run_decode_call(args, pa, runner, flush, wm, 0),
+                        "prefill": run_prefill(args, pa, runner, flush, wm, 1, write=False)}
+        torch.cuda.empty_cache()
+        out["long"] = run_decode_call(args, pa, runner, flush, W.long_decode(), 0)
+        torch.cuda.empty_cache()
+        peaks = measured_peaks(pa)
+        out["measured_peaks"] = peaks
+        out["roofline"]["frac_of_measured_read"] = round(
+            kern_gbs / peaks["hbm_stream_read_GB/s"], 4)
+        if "prefill" in out:
+            out["prefill"]["roofline"]["frac_of_measured_gemm"] = round(
+                out["prefill"]["value"] / peaks["bf16_gemm_TFLOP/s"], 4)
     if not args.no_cpu_baseline and not args.kv_fp8:
         sk = bench_sinks(args, w)
         out["cpu_baseline"] = cpu_baseline(w, sinks=None if sk is None else sk.cpu())

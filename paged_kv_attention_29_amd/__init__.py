@@ -107,6 +107,65 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+# ---- marshalling guards: the C entry points read raw device pointers, so a
+#      host tensor, a wrong integer width or a strided view would be read as
+#      something else.  These checks run before any C call and launch nothing.
+_INT32 = (torch.int32,)
+_INT64 = (torch.int64,)
+_F32 = (torch.float32,)
+_ATTN = (torch.float16, torch.bfloat16)
+_CACHE = (torch.float16, torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
+
+
+def _need(name: str, t, dtypes=None, contiguous: bool = False, optional: bool = False) -> None:
+    if t is None:
+        if optional:
+            return
+        raise TypeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, "
+                        f"got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_rows(name: str, t, dtypes) -> None:
+    """key/value of reshape_and_cache: any token stride, heads and head
+    elements contiguous inside a row."""
+    _need(name, t, dtypes)
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [tokens, num_kv_heads, head_size] with contiguous rows")
+
+
+def _same_dtype(name: str, t: Optional[torch.Tensor], ref: torch.Tensor) -> None:
+    if t is not None and t.dtype != ref.dtype:
+        raise TypeError(f"{name} must have the query's dtype {ref.dtype}, got {t.dtype}")
+
+
+def _need_cache(key_cache, value_cache) -> None:
+    _need("key_cache", key_cache, _CACHE, contiguous=True)
+    _need("value_cache", value_cache, _CACHE, contiguous=True)
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("key_cache and value_cache must have the same shape and dtype")
+    if key_cache.dim() != 4:
+        raise ValueError("caches must be [num_blocks, block_size, num_kv_heads, head_size]")
+
+
+def _need_table(block_table) -> None:
+    _need("block_table", block_table, _INT32)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be a 2-D int32 tensor with contiguous rows")
+
+
+def _need_scales(k_scale, v_scale) -> None:
+    _need("k_scale", k_scale, _F32, optional=True)
+    _need("v_scale", v_scale, _F32, optional=True)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -122,6 +181,12 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
     """Write key/value rows [i] into slot slot_mapping[i]; negative slots skip.
     A uint8 / float8_e4m3fn cache is quantised with the device fp32 scalars
     k_scale / v_scale."""
+    _need_rows("key", key, _ATTN)
+    _need_rows("value", value, _ATTN)
+    _same_dtype("value", value, key)
+    _need_cache(key_cache, value_cache)
+    _need("slot_mapping", slot_mapping, _INT64, contiguous=True)
+    _need_scales(k_scale, v_scale)
     nb, bs, hkv, d = key_cache.shape
     _check("reshape_and_cache", lib.reshape_and_cache(
         _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_cache),
@@ -139,6 +204,19 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        sinks: Optional[torch.Tensor] = None,
                        k_scale: Optional[torch.Tensor] = None,
                        v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need("q", q, _ATTN, contiguous=True)
+    _need("out", out, _ATTN, contiguous=True)
+    _same_dtype("out", out, q)
+    _need_cache(key_cache, value_cache)
+    _need("cu_seqlens_q", cu_seqlens_q, _INT32, contiguous=True)
+    _need("seq_lens", seq_lens, _INT32, contiguous=True)
+    _need_table(block_table)
+    _need("lse", lse, _F32, contiguous=True, optional=True)
+    _need("alibi_slopes", alibi_slopes, _F32, contiguous=True, optional=True)
+    _need("sinks", sinks, _F32, contiguous=True, optional=True)
+    _need_scales(k_scale, v_scale)
+    if cu_seqlens_q.numel() != seq_lens.numel() + 1:
+        raise ValueError("cu_seqlens_q must hold num_seqs + 1 entries")
     total_q, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     _check("paged_attn_prefill", lib.paged_attn_prefill(
@@ -161,6 +239,18 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
                       sinks: Optional[torch.Tensor] = None,
                       k_scale: Optional[torch.Tensor] = None,
                       v_scale: Optional[torch.Tensor] = None) -> None:
+    _need("q", q, _ATTN, contiguous=True)
+    _need("out", out, _ATTN, contiguous=True, optional=num_splits > 1)
+    _same_dtype("out", out, q)
+    _need_cache(key_cache, value_cache)
+    _need("seq_lens", seq_lens, _INT32, contiguous=True)
+    _need_table(block_table)
+    _need("lse", lse, _F32, contiguous=True, optional=True)
+    _need("part_out", part_out, _F32, contiguous=True, optional=num_splits <= 1)
+    _need("part_lse", part_lse, _F32, contiguous=True, optional=num_splits <= 1)
+    _need("alibi_slopes", alibi_slopes, _F32, contiguous=True, optional=True)
+    _need("sinks", sinks, _F32, contiguous=True, optional=True)
+    _need_scales(k_scale, v_scale)
     b, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     _check("paged_attn_decode", lib.paged_attn_decode(
@@ -174,6 +264,10 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
 def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: torch.Tensor,
                       out_lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """parts_out [S, T, H, D], parts_lse [S, H, T] -> out [T, H, D] (+ out_lse [H, T])."""
+    _need("out", out, _ATTN + _F32, contiguous=True)
+    _need("parts_out", parts_out, _ATTN + _F32, contiguous=True)
+    _need("parts_lse", parts_lse, _F32, contiguous=True)
+    _need("out_lse", out_lse, _F32, contiguous=True, optional=True)
     s, t, h, d = parts_out.shape
     _check("merge_attn_states", lib.merge_attn_states(
         _ptr(out), _ptr(out_lse), _ptr(parts_out), _ptr(parts_lse), s, t, h, d,
@@ -194,6 +288,16 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
     header).  ``workspace`` is (parts_out, parts_lse, work_ints) sized for
     max_prefix_splits + 1 parts; it is allocated here with torch when not
     given."""
+    _need("q", q, _ATTN, contiguous=True)
+    _need("out", out, _ATTN, contiguous=True)
+    _same_dtype("out", out, q)
+    _need_cache(key_cache, value_cache)
+    _need("cu_seqlens_q", cu_seqlens_q, _INT32, contiguous=True)
+    _need("seq_lens", seq_lens, _INT32, contiguous=True)
+    _need_table(block_table)
+    _need("lse", lse, _F32, contiguous=True, optional=True)
+    _need("sinks", sinks, _F32, contiguous=True, optional=True)
+    _need_scales(k_scale, v_scale)
     t, hq, d = q.shape
     nb, bs, hkv, _ = key_cache.shape
     b = seq_lens.numel()
@@ -203,6 +307,9 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                      torch.empty(n, hq, t, dtype=torch.float32, device=q.device),
                      torch.empty(b + 3, dtype=torch.int32, device=q.device))
     parts_out, parts_lse, ints = workspace
+    _need("workspace parts_out", parts_out, (q.dtype,), contiguous=True)
+    _need("workspace parts_lse", parts_lse, _F32, contiguous=True)
+    _need("workspace ints", ints, _INT32, contiguous=True)
     _check("paged_attn_cascade", lib.paged_attn_cascade(
         _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b, t, int(max_seqlen_q),
@@ -247,6 +354,11 @@ def check_indices(num_blocks: int, block_size: int, slot_mapping: Optional[torch
     if counts is None:
         dev = next(t for t in (slot_mapping, block_table, seq_lens) if t is not None).device
         counts = torch.empty(3, dtype=torch.int32, device=dev)
+    _need("slot_mapping", slot_mapping, _INT64, contiguous=True, optional=True)
+    _need("seq_lens", seq_lens, _INT32, contiguous=True, optional=True)
+    if block_table is not None:
+        _need_table(block_table)
+    _need("counts", counts, _INT32, contiguous=True)
     n_tok = 0 if slot_mapping is None else slot_mapping.numel()
     n_seq = 0 if seq_lens is None else seq_lens.numel()
     stride = 0 if block_table is None else block_table.stride(0)

@@ -32,6 +32,7 @@ class CallBuffers:
     lse: torch.Tensor
     part_out: Optional[torch.Tensor] = None
     part_lse: Optional[torch.Tensor] = None
+    causal: bool = True
 
 
 class PagedCache:
@@ -88,14 +89,14 @@ class PagedCache:
             seq_lens=torch.from_numpy(call.seq_lens.astype(np.int32)).to(dev),
             block_table=self.block_table.index_select(0, ids).contiguous(),
             max_seqlen_q=int(call.query_lens.max()), max_seqlen_k=int(call.seq_lens.max()),
-            num_splits=S, out=out, lse=lse, part_out=po, part_lse=pl)
+            num_splits=S, out=out, lse=lse, part_out=po, part_lse=pl, causal=bool(call.causal))
 
     def run(self, cb: CallBuffers, stream=None) -> None:
         w = self.w
         if cb.kind == "prefill":
             paged_attn_prefill(cb.out, cb.q, self.key_cache, self.value_cache, cb.cu_seqlens_q,
                                cb.seq_lens, cb.block_table, cb.max_seqlen_q, cb.max_seqlen_k,
-                               w.scale, True, w.window_left, w.softcap, self.alibi, lse=cb.lse,
+                               w.scale, cb.causal, w.window_left, w.softcap, self.alibi, lse=cb.lse,
                                stream=stream, sinks=self.sinks, k_scale=self.k_scale,
                                v_scale=self.v_scale)
         elif cb.num_splits == 1:

@@ -30,7 +30,7 @@ def oracle_call(w, kc, vc, call, num_splits=1):
     bt = torch.from_numpy(w.block_table[np.asarray(call.seq_ids)])
     if call.kind == "prefill":
         return oracle.attend(call.q, kc, vc, call.cu_seqlens_q.tolist(), call.seq_lens.tolist(),
-                             bt, w.scale, True, w.window_left, w.softcap, w.alibi_slopes)
+                             bt, w.scale, call.causal, w.window_left, w.softcap, w.alibi_slopes)
     if num_splits == 1:
         return oracle.decode(call.q, kc, vc, call.seq_lens.tolist(), bt, w.scale, w.window_left,
                              w.softcap, w.alibi_slopes)
@@ -66,6 +66,33 @@ def oracle_sampled(w, call, i: int, g: int):
     out, lse = oracle.attend(q, kc, vc, [0, r1 - r0], [L], table, w.scale, True, w.window_left,
                              w.softcap, slopes)
     return out, lse, (r0, r1), heads
+
+
+def oracle_sequence(w, call, i: int):
+    """Reference for every query head of sequence i of a call, computed on a
+    compact cache that holds only that sequence's blocks (all KV heads; built
+    with the oracle's own scatter, shuffled block ids).  Used where the whole
+    workload's cache is too large to replay at once on the host.
+    Returns (out [nq, Hq, D], lse [Hq, nq], rows)."""
+    b = int(call.seq_ids[i])
+    L = int(call.seq_lens[i])
+    bs = w.block_size
+    nblk = -(-L // bs)
+    perm = np.random.default_rng(7000 + b).permutation(nblk + 2)
+    table = torch.from_numpy(perm[:nblk].astype(np.int32))[None]
+    shape = (nblk + 2, bs, w.num_kv_heads, w.head_size)
+    kc = torch.full(shape, NAN, dtype=w.dtype)
+    vc = torch.full(shape, NAN, dtype=w.dtype)
+    k, v = w.sequence_kv(b, 0, L)
+    pos = np.arange(L)
+    slots = torch.from_numpy(perm[pos // bs].astype(np.int64) * bs + pos % bs)
+    oracle.scatter(k, v, slots, kc, vc)
+    del k, v
+    cu = call.cu_seqlens_q
+    r0, r1 = int(cu[i]), int(cu[i + 1])
+    out, lse = oracle.attend(call.q[r0:r1], kc, vc, [0, r1 - r0], [L], table, w.scale, True,
+                             w.window_left, w.softcap, w.alibi_slopes)
+    return out, lse, (r0, r1)
 
 
 def assert_attn_close(gpu_out, ref_out, what="out", max_abs=MAX_ABS, mean_abs=MEAN_ABS):

@@ -2,19 +2,35 @@
 and rejects invalid arguments on the host before touching a GPU (no GPU
 needed: every call here fails validation, so nothing is launched)."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_probe_validation(lib):
+    import ctypes
+    f = lib.lib.pa_probe_stream
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p]
+    assert f(3, 16, 16, 16, 1, 4, None) == -1          # unknown mode
+    assert f(0, 16, 16, 24, 1, 4, None) == -1          # not a multiple of 16 bytes
+    assert f(0, 16, 16, 16, 0, 4, None) == -1          # no workgroups
+    assert f(0, 16, 16, 16, 1, 3, None) == -1          # unsupported unroll
+    assert f(1, None, 16, 16, 1, 4, None) == -1        # copy without a source
+    assert f(0, 8, 16, 16, 1, 4, None) == -1           # misaligned
 
 
 def test_header_declares_the_four_entry_points():
@@ -160,3 +176,97 @@ def test_cascade_validation(lib, kw, code):
 def test_cascade_empty_is_noop(lib):
     assert _cascade(lib, num_seqs=0, q=None, kc=None, vc=None, seq_lens=None, bt=None, cu=None,
                     parts=None, parts_lse=None, ints=None) == 0
+
+
+# ----------------------------------------------------------------------------
+# the Python binding's marshalling guards (they raise before any C call)
+# ----------------------------------------------------------------------------
+def _as_gpu(t):
+    """A host tensor that claims to live on the GPU: it passes the device
+    check, so the dtype / layout guards after it can be exercised without a
+    GPU (each case below fails one of them, so no C call is made)."""
+    import torch
+
+    class OnGpu(torch.Tensor):
+        @property
+        def is_cuda(self):
+            return True
+
+    return t.as_subclass(OnGpu)
+
+
+def _decode_args(torch, **over):
+    a = dict(out=_as_gpu(torch.zeros(2, 4, 64, dtype=torch.float16)),
+             q=_as_gpu(torch.zeros(2, 4, 64, dtype=torch.float16)),
+             key_cache=_as_gpu(torch.zeros(8, 16, 2, 64, dtype=torch.float16)),
+             value_cache=_as_gpu(torch.zeros(8, 16, 2, 64, dtype=torch.float16)),
+             seq_lens=_as_gpu(torch.zeros(2, dtype=torch.int32)),
+             block_table=_as_gpu(torch.zeros(2, 4, dtype=torch.int32)),
+             max_seq_len=10, scale=0.125)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("field,make,exc", [
+    ("seq_lens", lambda torch: torch.zeros(2, dtype=torch.int64), TypeError),
+    ("block_table", lambda torch: torch.zeros(2, 4, dtype=torch.int64), TypeError),
+    ("q", lambda torch: torch.zeros(4, 2, 64, dtype=torch.float16).transpose(0, 1), ValueError),
+    ("out", lambda torch: torch.zeros(2, 4, 64, dtype=torch.bfloat16), TypeError),
+    ("lse", lambda torch: torch.zeros(4, 2, dtype=torch.float16), TypeError),
+    ("alibi_slopes", lambda torch: torch.zeros(4, dtype=torch.float64), TypeError),
+    ("key_cache", lambda torch: torch.zeros(8, 16, 2, 64, dtype=torch.float32), TypeError),
+])
+def test_binding_rejects_bad_decode_tensors(lib, field, make, exc):
+    import torch
+    a = _decode_args(torch, **{field: _as_gpu(make(torch))})
+    out, q, kc, vc, sl, bt = (a.pop(k) for k in ("out", "q", "key_cache", "value_cache",
+                                                 "seq_lens", "block_table"))
+    with pytest.raises(exc):
+        lib.paged_attn_decode(out, q, kc, vc, sl, bt, **a)
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    h = lambda *s, dt=torch.float16: torch.zeros(*s, dtype=dt)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lib.paged_attn_decode(h(2, 4, 64), h(2, 4, 64), h(8, 16, 2, 64), h(8, 16, 2, 64),
+                              h(2, dt=torch.int32), h(2, 4, dt=torch.int32), 10, 0.125)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lib.paged_attn_prefill(h(5, 4, 64), h(5, 4, 64), h(8, 16, 2, 64), h(8, 16, 2, 64),
+                               h(2, dt=torch.int32), h(1, dt=torch.int32), h(1, 4, dt=torch.int32),
+                               5, 23, 0.125)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lib.reshape_and_cache(h(5, 2, 64), h(5, 2, 64), h(8, 16, 2, 64), h(8, 16, 2, 64),
+                              h(5, dt=torch.int64))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lib.merge_attn_states(h(3, 4, 64), h(2, 3, 4, 64, dt=torch.float32),
+                              h(2, 4, 3, dt=torch.float32))
+
+
+def test_binding_rejects_bad_prefill_and_cache_tensors(lib):
+    import torch
+    g = lambda *s, dt=torch.float16: _as_gpu(torch.zeros(*s, dtype=dt))
+    cache = (g(8, 16, 2, 64), g(8, 16, 2, 64))
+    # cu_seqlens_q as int64 (torch.tensor's default for Python ints)
+    with pytest.raises(TypeError, match="cu_seqlens_q"):
+        lib.paged_attn_prefill(g(5, 4, 64), g(5, 4, 64), *cache, g(2, dt=torch.int64),
+                               g(1, dt=torch.int32), g(1, 4, dt=torch.int32), 5, 23, 0.125)
+    # cu_seqlens_q of the wrong length
+    with pytest.raises(ValueError, match="num_seqs"):
+        lib.paged_attn_prefill(g(5, 4, 64), g(5, 4, 64), *cache, g(3, dt=torch.int32),
+                               g(1, dt=torch.int32), g(1, 4, dt=torch.int32), 5, 23, 0.125)
+    # slot_mapping as int32
+    with pytest.raises(TypeError, match="slot_mapping"):
+        lib.reshape_and_cache(g(5, 2, 64), g(5, 2, 64), *cache, g(5, dt=torch.int32))
+    # key rows with a gap between heads
+    with pytest.raises(ValueError, match="contiguous rows"):
+        lib.reshape_and_cache(g(5, 2, 80)[:, :, :64], g(5, 2, 64), *cache, g(5, dt=torch.int64))
+    # mismatched K and V caches
+    with pytest.raises(ValueError, match="same shape"):
+        lib.reshape_and_cache(g(5, 2, 64), g(5, 2, 64), g(8, 16, 2, 64), g(9, 16, 2, 64),
+                              g(5, dt=torch.int64))
+    # split decode without fp32 partial buffers
+    with pytest.raises(TypeError, match="part_out"):
+        lib.paged_attn_decode(None, g(2, 4, 64), *cache, g(2, dt=torch.int32),
+                              g(2, 4, dt=torch.int32), 10, 0.125, num_splits=2,
+                              part_out=g(2, 2, 4, 64), part_lse=g(2, 4, 2, dt=torch.float32))
