@@ -133,12 +133,18 @@ def _need(name: str, t, dtypes=None, contiguous: bool = False, optional: bool = 
         raise ValueError(f"{name} must be contiguous")
 
 
-def _need_rows(name: str, t, dtypes) -> None:
-    """key/value of reshape_and_cache: any token stride, heads and head
-    elements contiguous inside a row."""
+def _need_rows(name: str, t, dtypes, row_elems: int) -> None:
+    """key/value of reshape_and_cache: [tokens, num_kv_heads, head_size] or
+    [tokens, num_kv_heads * head_size], any token stride, the row_elems
+    elements of a row contiguous."""
     _need(name, t, dtypes)
-    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
-        raise ValueError(f"{name} must be [tokens, num_kv_heads, head_size] with contiguous rows")
+    if t.dim() == 3:
+        ok = t.stride(2) == 1 and t.stride(1) == t.shape[2] and t.shape[1] * t.shape[2] == row_elems
+    else:
+        ok = t.dim() == 2 and t.stride(1) == 1 and t.shape[1] == row_elems
+    if not ok:
+        raise ValueError(f"{name} must be [tokens, num_kv_heads, head_size] rows matching the "
+                         f"cache, each row contiguous")
 
 
 def _same_dtype(name: str, t: Optional[torch.Tensor], ref: torch.Tensor) -> None:
@@ -181,10 +187,10 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
     """Write key/value rows [i] into slot slot_mapping[i]; negative slots skip.
     A uint8 / float8_e4m3fn cache is quantised with the device fp32 scalars
     k_scale / v_scale."""
-    _need_rows("key", key, _ATTN)
-    _need_rows("value", value, _ATTN)
-    _same_dtype("value", value, key)
     _need_cache(key_cache, value_cache)
+    _need_rows("key", key, _ATTN, key_cache.shape[2] * key_cache.shape[3])
+    _need_rows("value", value, _ATTN, key_cache.shape[2] * key_cache.shape[3])
+    _same_dtype("value", value, key)
     _need("slot_mapping", slot_mapping, _INT64, contiguous=True)
     _need_scales(k_scale, v_scale)
     nb, bs, hkv, d = key_cache.shape

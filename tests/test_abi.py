@@ -259,7 +259,7 @@ def test_binding_rejects_bad_prefill_and_cache_tensors(lib):
     with pytest.raises(TypeError, match="slot_mapping"):
         lib.reshape_and_cache(g(5, 2, 64), g(5, 2, 64), *cache, g(5, dt=torch.int32))
     # key rows with a gap between heads
-    with pytest.raises(ValueError, match="contiguous rows"):
+    with pytest.raises(ValueError, match="each row contiguous"):
         lib.reshape_and_cache(g(5, 2, 80)[:, :, :64], g(5, 2, 64), *cache, g(5, dt=torch.int64))
     # mismatched K and V caches
     with pytest.raises(ValueError, match="same shape"):
