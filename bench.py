@@ -131,14 +131,26 @@ class Timed:
 
 
 class Flush:
-    """A 512 MiB device buffer written (a fill kernel) between timed
-    repetitions, outside the timed region."""
+    """A 512 MiB device buffer streamed through between timed repetitions,
+    outside the timed region.  It is READ (pa_probe_stream), not written: a
+    write leaves up to L2 + Infinity Cache worth of dirty lines (about
+    290 MB) whose write-back then competes with the next timed kernel's own
+    traffic, while a read evicts with clean lines."""
 
-    def __init__(self):
-        self.buf = torch.empty(SCRATCH_MIB << 18, dtype=torch.float32, device="cuda")
+    def __init__(self, pa):
+        import ctypes
+        self.f = pa.lib.pa_probe_stream
+        self.f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        self.f.restype = ctypes.c_int
+        self.buf = torch.ones(SCRATCH_MIB << 18, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
 
     def __call__(self):
-        self.buf.zero_()
+        rc = self.f(0, self.buf.data_ptr(), self.sink.data_ptr(), self.buf.numel() * 4, 2048, 4,
+                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, rc
 
 
 def run_decode(args, pa, runner, w):
@@ -675,7 +687,7 @@ def main():
                          digest),
                      "kernel": "paged_attn_decode", "bytes_per_launch": r["bytes"]},
     }
-    flush = Flush()
+    flush = Flush(pa)
     if not args.no_prefill and args.workload == "decode":
         out["prefill"] = run_prefill(args, pa, runner, flush)
     if not args.no_extra and args.workload == "decode":

@@ -135,14 +135,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 // exp2 of a finite-or--inf argument (v_exp_f32); exp2(-inf) = 0
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh from exp: tanh(x) = sign(x) * (1 - 2 / (exp(2|x|) + 1)) with the
-// hardware exp2 and reciprocal; exact limits at +-inf, absolute error a few
-// ulp of 1 near 0.
-__device__ __forceinline__ float tanh_f32(float x) {
-  float ax = fabsf(x);
-  float e = fast_exp2(2.0f * kLog2e * ax);
-  float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-  return copysignf(t, x);
+// Soft-capped logit in log2 units, cap * tanh(scale * s / cap) * log2(e),
+// with tanh(x) = 1 - 2 / (1 + e^{2x}) on the hardware exp2 and reciprocal:
+// the limits are exact (exp2 overflows to inf and its reciprocal to 0 for
+// large x; it underflows to 0 for very negative x), and the absolute error
+// of tanh is a few ulp of 1.  Five instructions: mul, exp2, add, rcp, fma.
+// k2 = 2 * log2(e) * scale / cap, cap_log2 = cap * log2(e).
+__device__ __forceinline__ float softcap_log2(float s, float k2, float cap_log2) {
+  const float r = __builtin_amdgcn_rcpf(1.0f + fast_exp2(s * k2));
+  return fmaf(r, -2.0f * cap_log2, cap_log2);
 }
 
 // floor(j / d) for 0 <= j < 2^24 and 16 <= d <= 256, with

@@ -50,7 +50,7 @@ struct DecodeArgs {
   int chunk;            // keys per split (block-aligned, from the batch bound)
   uint32_t bs_magic;    // ceil(2^32 / bs)
   float scale_log2;     // scale * log2(e)
-  float scale_over_cap; // scale / softcap
+  float cap_k2;         // 2 log2(e) scale / softcap
   float cap_log2;       // softcap * log2(e)
   int window_left;      // -1 = none
   const float* alibi;   // nullable
@@ -412,7 +412,7 @@ struct Dec {
       for (int e = 0; e < 4; ++e) {
         const int key = j0 + 4 * c4 + e;
         float v;
-        if constexpr (SOFTCAP) v = a.cap_log2 * tanh_f32(sc[e] * a.scale_over_cap);
+        if constexpr (SOFTCAP) v = softcap_log2(sc[e], a.cap_k2, a.cap_log2);
         else v = sc[e] * a.scale_log2;
         if constexpr (ALIBI) v -= slope_log2 * static_cast<float>(it.pos - key);
         x[nt][e] = (key >= it.lo_vis && key < it.hi) ? v : kNegInf;
@@ -428,8 +428,11 @@ struct Dec {
       const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
       l_run *= alpha;
+      // columns whose reference is still -inf hold zeros (no key seen yet)
+      if (wave_any(grow && m_run != kNegInf)) {
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) o[dc] *= alpha;
+        for (int dc = 0; dc < DC; ++dc) o[dc] *= alpha;
+      }
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.0f : m_run;
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
     // the K scale multiplies every score
     const float ks = *a.k_scale;
     a.scale_log2 *= ks;
-    a.scale_over_cap *= ks;
+    a.cap_k2 *= ks;
   }
 
   const int lane = threadIdx.x & 63;
@@ -754,7 +757,7 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.bs_magic = static_cast<uint32_t>(((1ULL << 32) + p.block_size - 1) / p.block_size);
   const bool softcap = p.softcap > 0.f;
   a.scale_log2 = p.scale * kLog2e;
-  a.scale_over_cap = softcap ? p.scale / p.softcap : 0.f;
+  a.cap_k2 = softcap ? 2.0f * kLog2e * p.scale / p.softcap : 0.f;
   a.cap_log2 = p.softcap * kLog2e;
   a.window_left = p.window_left;
   a.alibi = p.alibi_slopes;

@@ -65,7 +65,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, G, bs, tok_per_tile, n_qtiles;
   uint32_t bs_magic;
   float scale_log2;     // scale * log2(e)
-  float scale_over_cap; // scale / softcap
+  float cap_k2;         // 2 log2(e) scale / softcap
   float cap_log2;       // softcap * log2(e)
   int causal, window_left;
   const float* alibi;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     // the K scale multiplies every score, the V scale the result
     const float ks = *a.k_scale;
     a.scale_log2 *= ks;
-    a.scale_over_cap *= ks;
+    a.cap_k2 *= ks;
     v_scale = *a.v_scale;
   }
 
@@ -404,21 +404,32 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       for (int e = 0; e < 16; ++e) {
         float z = sacc[h2][e];
         const int key = kbase + 32 * h2 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-        if constexpr (SOFTCAP) z = a.cap_log2 * tanh_f32(z * a.scale_over_cap);
+        if constexpr (SOFTCAP) z = softcap_log2(z, a.cap_k2, a.cap_log2);
         else if constexpr (ALIBI) z = z * a.scale_log2;
         if constexpr (ALIBI) z -= slope_log2 * static_cast<float>(abs(pos - key));
         sacc[h2][e] = z;
       }
     if (need_mask) {
-      // visible iff 0 <= key - lo_row <= span_row (unsigned compare)
-      const int base = kbase + 4 * g2 - lo_row;
+      if (a.window_left < 0) {
+        // one bound (no window): the key at offset o of the lane's pattern is
+        // visible iff o <= hi_row - kbase - 4*g2 (o is an inline constant)
+        const int lim = hi_row - kbase - 4 * g2;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t rel = static_cast<uint32_t>(base + 32 * h2 + 8 * (e >> 2) + (e & 3));
-          sacc[h2][e] = rel <= span_row ? sacc[h2][e] : kNegInf;
-        }
+          for (int e = 0; e < 16; ++e)
+            sacc[h2][e] = 32 * h2 + 8 * (e >> 2) + (e & 3) <= lim ? sacc[h2][e] : kNegInf;
+      } else {
+        // visible iff 0 <= key - lo_row <= span_row (unsigned compare)
+        const int base = kbase + 4 * g2 - lo_row;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t rel = static_cast<uint32_t>(base + 32 * h2 + 8 * (e >> 2) + (e & 3));
+            sacc[h2][e] = rel <= span_row ? sacc[h2][e] : kNegInf;
+          }
+      }
     }
     // row max: a max3 tree over the lane's 32 scores, then the other half of
     // the row (lane ^ 32) through a lane swap
@@ -445,8 +456,13 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       const float m_new = grow ? m_tile : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
       l_run *= alpha;
+      // a row whose reference is still -inf has seen no key and holds zeros:
+      // the accumulators need no scaling when every growing row is such a row
+      // (the first tile of a wave)
+      if (wave_any(grow && m_run != kNegInf)) {
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
+        for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
+      }
       m_run = m_new;
     }
     const float neg_m = m_run == kNegInf ? 0.0f : -m_run;
@@ -615,7 +631,6 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
 
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
   float l_tot = l_run + shfl_xor(l_run, 32);
-  if (!row_ok) return;
   float m_fin = m_run, o_scale = 1.0f;
   if (a.sinks != nullptr && blockIdx.z == 0) {
     // the sink as one more state (max sk, sum 1, output 0)
@@ -628,21 +643,44 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     }
   }
   const float inv = l_tot > 0.f ? o_scale * v_scale * __builtin_amdgcn_rcpf(l_tot) : 0.0f;
-  const int64_t qrow = q0 + tok0 + tk;
   const int64_t part = blockIdx.z;  // key split (0 without splits)
-  uint16_t* orow = a.out + ((part * a.total_q + qrow) * a.Hq + head) * D + 4 * g2;
+  // The wave's 32 output rows go through LDS (the ring is idle: every wave
+  // passed the loop's last barrier and no DMA is in flight) so that the
+  // global stores write whole rows, 16 bytes per lane: stored straight from
+  // the accumulator layout, each store instruction would touch 32 rows with
+  // 16 bytes apiece.
+  constexpr int OP = D + 8;  // LDS row pitch in elements (16-byte pad)
+  static_assert((size_t)kNW<D> * 32 * OP * 2 <= prefill_lds_bytes<D, false>(), "epilogue staging");
+  uint16_t* ost = reinterpret_cast<uint16_t*>(smem) + wave * 32 * OP;
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       const v16f& v = oacc[dc];
-      u32x2 w = {T::pack2(v[4 * e4] * inv, v[4 * e4 + 1] * inv),
-                 T::pack2(v[4 * e4 + 2] * inv, v[4 * e4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + dc * 32 + 8 * e4) = w;
+      const u32x2 w = {T::pack2(v[4 * e4] * inv, v[4 * e4 + 1] * inv),
+                       T::pack2(v[4 * e4 + 2] * inv, v[4 * e4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(ost + r32 * OP + dc * 32 + 8 * e4 + 4 * g2) = w;
     }
-  if (a.lse != nullptr && g2 == 0)
+  wave_lds_sync();
+  constexpr int LPR = D / 8;     // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / LPR;  // row of the wave
+    const int c = (lane % LPR) * 8;
+    const v8s val = *reinterpret_cast<const v8s*>(ost + r * OP + c);
+    const int rr = wave * 32 + r;
+    const int tk_r = rr / a.G;
+    if (tk_r < ntok) {
+      const int64_t qr = q0 + tok0 + tk_r;
+      *reinterpret_cast<v8s*>(a.out + ((part * a.total_q + qr) * a.Hq + g * a.G + (rr - tk_r * a.G)) * D + c) = val;
+    }
+  }
+  if (a.lse != nullptr && g2 == 0 && row_ok) {
+    const int64_t qrow = q0 + tok0 + tk;
     a.lse[(part * a.Hq + head) * a.total_q + qrow] =
         l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
 }
 
 template <typename T, int D, int FEAT>
@@ -708,7 +746,7 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.tok_per_tile = 0;  // set from the head size at launch
   const bool softcap = p.softcap > 0.f;
   a.scale_log2 = p.scale * kLog2e;
-  a.scale_over_cap = softcap ? p.scale / p.softcap : 0.f;
+  a.cap_k2 = softcap ? 2.0f * kLog2e * p.scale / p.softcap : 0.f;
   a.cap_log2 = p.softcap * kLog2e;
   a.causal = p.causal;
   a.window_left = p.window_left;
