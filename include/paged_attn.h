@@ -14,7 +14,8 @@
  *  - Tensor pointers are DEVICE pointers, except where a parameter says
  *    otherwise.  Integer sizes and scalars are passed by value from the host.
  *  - The caller owns every buffer, outputs included; the library allocates
- *    nothing and keeps no state between calls.
+ *    nothing and keeps no state between calls (the one exception is the
+ *    fixed scratch array of paged_attn_decode_noalloc, below).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and the call returns without synchronising.
  *  - Return value: PA_OK, or a negative code.  Arguments are validated on the
@@ -193,6 +194,38 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
                       const float* sinks, int num_splits, pa_dtype_t dtype,
                       pa_dtype_t kv_cache_dtype, const float* k_scale,
                       const float* v_scale, void* stream);
+
+/*
+ * paged_attn_decode_noalloc — for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): paged_attn_decode with num_splits parts followed by
+ * merge_attn_states into out / lse, with the fp32 partial results kept in a
+ * fixed device array of the library instead of caller workspace.  Nothing
+ * is allocated by the call.
+ *
+ *   Arguments as for paged_attn_decode without part_out / part_lse; out is
+ *   required and receives the merged result [num_seqs, num_heads, head_size]
+ *   (dtype), lse (nullable) fp32 [num_heads, num_seqs].  num_splits == 1
+ *   writes out directly and uses no scratch.
+ *   Limit: num_splits * num_seqs * num_heads * (head_size + 1) * 4 bytes (plus
+ *   up to 255 bytes of alignment) must fit the 32 MiB scratch, else
+ *   PA_ERR_UNSUPPORTED and nothing is enqueued.
+ *   The scratch is one array per GPU, held until the process ends and
+ *   shared by every call on that GPU: calls that overlap on one GPU (two
+ *   streams, or two threads) race on it.  Its contents are fully rewritten
+ *   by each call before they are read; nothing needs clearing.
+ */
+int paged_attn_decode_noalloc(void* out, float* lse, const void* q,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* seq_lens, const int32_t* block_table,
+                              int64_t block_table_stride, int num_seqs,
+                              int max_seq_len, int num_heads, int num_kv_heads,
+                              int head_size, int block_size, int64_t num_blocks,
+                              float scale, int window_left, float softcap,
+                              const float* alibi_slopes, const float* sinks,
+                              int num_splits, pa_dtype_t dtype,
+                              pa_dtype_t kv_cache_dtype, const float* k_scale,
+                              const float* v_scale, void* stream);
 
 /*
  * merge_attn_states — combine partial attention results by their

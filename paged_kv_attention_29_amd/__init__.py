@@ -28,6 +28,7 @@ __all__ = [
     "reshape_and_cache",
     "paged_attn_prefill",
     "paged_attn_decode",
+    "paged_attn_decode_noalloc",
     "merge_attn_states",
     "paged_attn_cascade",
     "local_virtual_batches",
@@ -64,6 +65,9 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
                                       _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.paged_attn_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
+                                              _vp, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
     lib.pa_check_indices.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i32, _vp, _vp]
     lib.paged_attn_cascade.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
@@ -71,7 +75,8 @@ def _load() -> ctypes.CDLL:
                                        _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
     lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
                                              _vp, _vp, _vp]
-    for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode", "merge_attn_states",
+    for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode",
+               "paged_attn_decode_noalloc", "merge_attn_states",
                "pa_check_indices", "paged_attn_cascade", "pa_local_virtual_batches"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
@@ -265,6 +270,38 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
         int(max_seq_len), hq, hkv, d, bs, nb, float(scale), int(window_left), float(softcap),
         _ptr(alibi_slopes), _ptr(sinks), int(num_splits), _code(q.dtype), _code(key_cache.dtype),
         _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                              value_cache: torch.Tensor, seq_lens: torch.Tensor,
+                              block_table: torch.Tensor, max_seq_len: int, scale: float,
+                              window_left: int = -1, softcap: float = 0.0,
+                              alibi_slopes: Optional[torch.Tensor] = None, num_splits: int = 1,
+                              lse: Optional[torch.Tensor] = None, stream=None,
+                              sinks: Optional[torch.Tensor] = None,
+                              k_scale: Optional[torch.Tensor] = None,
+                              v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Split decode + merge into ``out`` with the partials in the library's
+    fixed device scratch (no allocation; see the header for the limit)."""
+    _need("q", q, _ATTN, contiguous=True)
+    _need("out", out, _ATTN, contiguous=True)
+    _same_dtype("out", out, q)
+    _need_cache(key_cache, value_cache)
+    _need("seq_lens", seq_lens, _INT32, contiguous=True)
+    _need_table(block_table)
+    _need("lse", lse, _F32, contiguous=True, optional=True)
+    _need("alibi_slopes", alibi_slopes, _F32, contiguous=True, optional=True)
+    _need("sinks", sinks, _F32, contiguous=True, optional=True)
+    _need_scales(k_scale, v_scale)
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = key_cache.shape
+    _check("paged_attn_decode_noalloc", lib.paged_attn_decode_noalloc(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(seq_lens),
+        _ptr(block_table), block_table.stride(0), b, int(max_seq_len), hq, hkv, d, bs, nb,
+        float(scale), int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks),
+        int(num_splits), _code(q.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale),
+        _stream(stream)))
+    return out
 
 
 def merge_attn_states(out: torch.Tensor, parts_out: torch.Tensor, parts_lse: torch.Tensor,

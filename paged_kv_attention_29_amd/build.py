@@ -13,7 +13,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "reshape_and_cache.hip", "merge.hip", "decode.hip", "prefill.hip",
-           "check.hip", "cascade.hip", "local.hip", "probe.hip"]
+           "check.hip", "cascade.hip", "local.hip", "probe.hip", "noalloc.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # never let the compiler form packed fp32 arithmetic

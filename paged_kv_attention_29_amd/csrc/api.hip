@@ -99,6 +99,72 @@ int check_kv(const char* fn, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype, const 
   return PA_OK;
 }
 
+// Checks shared by the decode entry points (paged_attn_decode and its
+// no-allocation variant).
+int check_decode(const char* fn, int num_seqs, int max_seq_len, int num_heads, int num_kv_heads,
+                 int head_size, int block_size, int64_t num_blocks, float scale, int window_left,
+                 float softcap, int num_splits, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
+                 const float* k_scale, const float* v_scale, const void* q,
+                 const void* key_cache, const void* value_cache, const int32_t* seq_lens,
+                 const int32_t* block_table, int64_t block_table_stride) {
+  int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, scale, window_left, softcap, dtype, q, key_cache,
+                             value_cache, seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
+  if (rc != PA_OK) return rc;
+  if (num_splits < 1 || num_splits > 256)
+    return fail(PA_ERR_INVALID, "%s: num_splits must be in [1, 256] (got %d)", fn, num_splits);
+  if (num_heads / num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
+  if (max_seq_len < 0) return fail(PA_ERR_INVALID, "%s: max_seq_len must be >= 0", fn);
+  if (max_seq_len >= (1 << 24))
+    return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
+  return PA_OK;
+}
+
+pa::AttnParams decode_params(void* out, float* lse, float* part_out, float* part_lse,
+                             const void* q, const void* key_cache, const void* value_cache,
+                             const int32_t* seq_lens, const int32_t* block_table,
+                             int64_t block_table_stride, int num_seqs, int max_seq_len,
+                             int num_heads, int num_kv_heads, int head_size, int block_size,
+                             float scale, int window_left, float softcap,
+                             const float* alibi_slopes, const float* sinks, int num_splits,
+                             pa_dtype_t dtype, pa_dtype_t kv_cache_dtype, const float* k_scale,
+                             const float* v_scale) {
+  pa::AttnParams p{};
+  p.out = out;
+  p.lse = lse;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.q = q;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.block_table_stride = block_table_stride;
+  p.num_seqs = num_seqs;
+  p.total_q = num_seqs;
+  p.max_seqlen_q = 1;
+  p.max_seqlen_k = max_seq_len;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_size = head_size;
+  p.block_size = block_size;
+  p.scale = scale;
+  p.causal = 1;
+  p.window_left = window_left;
+  p.softcap = softcap;
+  p.alibi_slopes = alibi_slopes;
+  p.sinks = sinks;
+  p.num_splits = num_splits;
+  p.dtype = static_cast<pa::Dtype>(dtype);
+  p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,55 +277,73 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
                       int num_splits, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
                       const float* k_scale, const float* v_scale, void* stream) {
   const char* fn = "paged_attn_decode";
-  int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
-                             num_blocks, scale, window_left, softcap, dtype, q, key_cache,
-                             value_cache, seq_lens, block_table, block_table_stride);
+  int rc = check_decode(fn, num_seqs, max_seq_len, num_heads, num_kv_heads, head_size, block_size,
+                        num_blocks, scale, window_left, softcap, num_splits, dtype,
+                        kv_cache_dtype, k_scale, v_scale, q, key_cache, value_cache, seq_lens,
+                        block_table, block_table_stride);
   if (rc != PA_OK) return rc;
-  rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
-  if (rc != PA_OK) return rc;
-  if (num_splits < 1 || num_splits > 256)
-    return fail(PA_ERR_INVALID, "%s: num_splits must be in [1, 256] (got %d)", fn, num_splits);
   if (num_splits == 1 && out == nullptr)
     return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (num_splits > 1 && (part_out == nullptr || part_lse == nullptr))
     return fail(PA_ERR_INVALID, "%s: num_splits > 1 needs part_out and part_lse", fn);
-  if (num_heads / num_kv_heads > 16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
-  if (max_seq_len < 0) return fail(PA_ERR_INVALID, "%s: max_seq_len must be >= 0", fn);
-  if (max_seq_len >= (1 << 24))
-    return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
   if (num_seqs == 0) return ok();
-  pa::AttnParams p{};
-  p.out = out;
-  p.lse = lse;
-  p.part_out = part_out;
-  p.part_lse = part_lse;
-  p.q = q;
-  p.key_cache = key_cache;
-  p.value_cache = value_cache;
-  p.seq_lens = seq_lens;
-  p.block_table = block_table;
-  p.block_table_stride = block_table_stride;
-  p.num_seqs = num_seqs;
-  p.total_q = num_seqs;
-  p.max_seqlen_q = 1;
-  p.max_seqlen_k = max_seq_len;
-  p.num_heads = num_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.head_size = head_size;
-  p.block_size = block_size;
-  p.scale = scale;
-  p.causal = 1;
-  p.window_left = window_left;
-  p.softcap = softcap;
-  p.alibi_slopes = alibi_slopes;
-  p.sinks = sinks;
-  p.num_splits = num_splits;
-  p.dtype = static_cast<pa::Dtype>(dtype);
-  p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
-  p.k_scale = k_scale;
-  p.v_scale = v_scale;
+  pa::AttnParams p = decode_params(out, lse, part_out, part_lse, q, key_cache, value_cache,
+                                   seq_lens, block_table, block_table_stride, num_seqs,
+                                   max_seq_len, num_heads, num_kv_heads, head_size, block_size,
+                                   scale, window_left, softcap, alibi_slopes, sinks, num_splits,
+                                   dtype, kv_cache_dtype, k_scale, v_scale);
   return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+int paged_attn_decode_noalloc(void* out, float* lse, const void* q, const void* key_cache,
+                              const void* value_cache, const int32_t* seq_lens,
+                              const int32_t* block_table, int64_t block_table_stride,
+                              int num_seqs, int max_seq_len, int num_heads, int num_kv_heads,
+                              int head_size, int block_size, int64_t num_blocks, float scale,
+                              int window_left, float softcap, const float* alibi_slopes,
+                              const float* sinks, int num_splits, pa_dtype_t dtype,
+                              pa_dtype_t kv_cache_dtype, const float* k_scale,
+                              const float* v_scale, void* stream) {
+  const char* fn = "paged_attn_decode_noalloc";
+  int rc = check_decode(fn, num_seqs, max_seq_len, num_heads, num_kv_heads, head_size, block_size,
+                        num_blocks, scale, window_left, softcap, num_splits, dtype,
+                        kv_cache_dtype, k_scale, v_scale, q, key_cache, value_cache, seq_lens,
+                        block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
+  // partial results [S, B, Hq, D] fp32, then their LSEs [S, Hq, B] at a
+  // 256-byte boundary
+  const size_t parts = (size_t)num_splits * num_seqs * num_heads * head_size * 4;
+  const size_t lse_off = (parts + 255) / 256 * 256;
+  const size_t need = num_splits > 1 ? lse_off + (size_t)num_splits * num_heads * num_seqs * 4 : 0;
+  if (need > pa::kNoallocScratchBytes)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: %d splits x %d sequences x %d heads x %d need %zu bytes of partial results; "
+                "the fixed scratch holds %zu",
+                fn, num_splits, num_seqs, num_heads, head_size, need, pa::kNoallocScratchBytes);
+  if (num_seqs == 0) return ok();
+  float* part_out = nullptr;
+  float* part_lse = nullptr;
+  if (num_splits > 1) {
+    void* base = nullptr;
+    if (pa::noalloc_scratch(&base) != 0)
+      return fail(PA_ERR_HIP, "%s: the device address of the scratch array is unavailable: %s",
+                  fn, hipGetErrorString(hipGetLastError()));
+    part_out = static_cast<float*>(base);
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(base) + lse_off);
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  pa::AttnParams p = decode_params(num_splits > 1 ? nullptr : out, num_splits > 1 ? nullptr : lse,
+                                   part_out, part_lse, q, key_cache, value_cache, seq_lens,
+                                   block_table, block_table_stride, num_seqs, max_seq_len,
+                                   num_heads, num_kv_heads, head_size, block_size, scale,
+                                   window_left, softcap, alibi_slopes, sinks, num_splits, dtype,
+                                   kv_cache_dtype, k_scale, v_scale);
+  rc = pa::launch_decode(p, st);
+  if (rc == 0 && num_splits > 1)
+    rc = pa::launch_merge(out, lse, part_out, part_lse, num_splits, num_seqs, num_heads,
+                          head_size, pa::kF32, static_cast<pa::Dtype>(dtype), st);
+  return hip_result(rc, fn);
 }
 
 int merge_attn_states(void* out, float* out_lse, const void* parts_out, const float* parts_lse,

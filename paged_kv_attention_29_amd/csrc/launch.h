@@ -61,6 +61,13 @@ struct AttnParams {
 
 int launch_decode(const AttnParams& p, hipStream_t stream);
 
+// Fixed per-device scratch of the no-allocation decode entry point: split
+// partial results (fp32 outputs, then their LSEs), at most this many bytes.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+// Device address of the calling thread's current device's scratch array
+// (looked up once per device).  Returns 0, or -3 when HIP reports an error.
+int noalloc_scratch(void** ptr);
+
 // host-side rewriting for chunked local attention; returns the number of
 // virtual sequences (outputs NULL: count only)
 int local_virtual_batches(int chunk, int block_size, const int32_t* qsl, const int32_t* seq_lens,
