@@ -21,7 +21,9 @@ mathematics independent of this code:
 * ``fp8``            — e4m3 code table and quantiser against torch's
                         float8_e4m3fn type, closed-form codes, the rounding
                         error bound.  An fp8 cache is attended by passing
-                        its dequantised float64 copy to ``attend``.
+                        its dequantised float64 copy to ``attend``; an fp8
+                        query (``scaled_fp8_quant``) likewise through
+                        ``dequantize_query``.
 
 Readings the pages leave open (softcap/ALiBi order, ALiBi slope index,
 window edge) are fixed by the readings documented with each function; they

@@ -20,8 +20,18 @@ descale arguments].  The arithmetic is not printed.  Readings used here:
   round to zero give the code 0x80); NaN gives 0x7F with the element's sign;
 * the dequantised element is value(code) * scale (a descale multiplies).
 
-The query is not quantised here (the page quantises it only for kernels
-that take an fp8 query; this build keeps the query in 16 bits).
+The query: with an fp8 cache the page quantises the query too, per tensor
+with the static scale ``layer._q_scale`` (``ops.scaled_fp8_quant(query,
+layer._q_scale)``), and passes that scale to the attention call as
+``q_descale`` beside k_descale / v_descale  [vLLM flash_attn.py (v0.9.0.1
+docs), FlashAttentionImpl.forward, the fp8 branch; vLLM flash_attn.py
+(e2f56c3), "queries are quantized in the attention layer" and the
+q_descale argument].  Reading used here: the query codes are made exactly
+as the cache codes are (``e4m3_quantize(q, q_scale)``), and the attention
+reads value(code) * q_scale, so attention with an fp8 query is attention
+over the dequantised query (``scaled_fp8_quant`` / ``dequantize_query``).
+Keeping the query in 16 bits (another backend's option) is plain attention
+with the unquantised query.
 """
 from __future__ import annotations
 
@@ -84,3 +94,17 @@ def scatter_fp8(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tens
         blk, off = divmod(int(s), bs)
         key_cache[blk, off] = e4m3_quantize(key[i], k_scale)
         value_cache[blk, off] = e4m3_quantize(value[i], v_scale)
+
+
+def scaled_fp8_quant(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """The query quantiser with a static per-tensor scale: uint8 e4m3 codes
+    of x / scale, the same arithmetic as the cache codes (see the module
+    readings)  [vLLM flash_attn.py (v0.9.0.1 docs), FlashAttentionImpl
+    .forward, ops.scaled_fp8_quant(query, layer._q_scale)]."""
+    return e4m3_quantize(x, scale)
+
+
+def dequantize_query(codes: torch.Tensor, q_scale: float) -> torch.Tensor:
+    """What the attention reads from an fp8 query: value(code) * q_scale
+    (q_descale), float64, for ``attend`` / ``decode``."""
+    return e4m3_dequantize(codes, q_scale)

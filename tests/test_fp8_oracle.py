@@ -86,3 +86,74 @@ def test_scatter_fp8_writes_codes_and_skips_padding():
     assert torch.equal(kc[1, 1], e4m3_quantize(key[0], 0.25))
     assert torch.equal(vc[2, 3], e4m3_quantize(val[3], 0.5))
     assert torch.equal(kc[0, 1], torch.zeros(2, 8, dtype=torch.uint8))   # slot of the padding row untouched
+
+
+# ----------------------------------------------------------------------------
+# the quantised query (an fp8 query with q_descale)
+# ----------------------------------------------------------------------------
+def test_query_quantiser_matches_torch_float8():
+    from oracle.fp8 import scaled_fp8_quant
+    g = torch.Generator().manual_seed(11)
+    q = (torch.randn(7, 4, 64, generator=g) * 3).to(torch.bfloat16)
+    for scale in (0.0125, 0.02, 1.0 / 64):
+        assert torch.equal(scaled_fp8_quant(q, scale), _torch_quantize(q, scale))
+
+
+def test_lossless_query_codes_give_the_16bit_attention():
+    """A query whose elements are e4m3 values times a power-of-two scale
+    quantises without loss, so attention through the fp8-query path equals
+    attention with the 16-bit query exactly."""
+    import oracle
+    from oracle.fp8 import dequantize_query, scaled_fp8_quant
+    g = torch.Generator().manual_seed(12)
+    q_scale = 2.0 ** -5
+    codes = torch.randint(0, 126, (3, 4, 64), generator=g, dtype=torch.uint8)
+    codes |= (torch.rand(3, 4, 64, generator=g) < 0.5).to(torch.uint8) << 7
+    q16 = (e4m3_values()[codes.long()] * q_scale).to(torch.bfloat16)
+    assert torch.equal(q16.double(), e4m3_values()[codes.long()] * q_scale)   # exact in bf16
+    assert torch.equal(scaled_fp8_quant(q16, q_scale) & 0x7F, codes & 0x7F)
+    kc = torch.randn(4, 16, 2, 64, generator=g).to(torch.bfloat16)
+    vc = torch.randn(4, 16, 2, 64, generator=g).to(torch.bfloat16)
+    bt = torch.tensor([[0, 1], [2, 3]], dtype=torch.int32)
+    args = (kc, vc, [0, 1, 3], [20, 31], bt, 0.125)
+    qd = dequantize_query(scaled_fp8_quant(q16, q_scale), q_scale)
+    o8, l8 = oracle.attend(qd, *args)
+    o16, l16 = oracle.attend(q16, *args)
+    assert torch.equal(o8, o16) and torch.equal(l8, l16)
+
+
+def test_fp8_query_attention_by_brute_force():
+    """Tiny fp8 case (fp8 query, fp8 cache) against a pure-Python loop that
+    quantises through torch's float8_e4m3fn type and multiplies the
+    descales in, one score at a time."""
+    import oracle
+    from oracle.fp8 import dequantize_query, scaled_fp8_quant
+    g = torch.Generator().manual_seed(13)
+    Hq, Hkv, D, bs, L = 4, 2, 8, 16, 21
+    q_scale, k_scale, v_scale, scale = 0.011, 0.023, 0.017, D ** -0.5
+    q = torch.randn(1, Hq, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(L, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(L, Hkv, D, generator=g).to(torch.bfloat16)
+    kc = torch.zeros(2, bs, Hkv, D, dtype=torch.uint8)
+    vc = torch.zeros(2, bs, Hkv, D, dtype=torch.uint8)
+    scatter_fp8(k, v, torch.arange(L), kc, vc, k_scale, v_scale)
+    bt = torch.tensor([[0, 1]], dtype=torch.int32)
+    qd = dequantize_query(scaled_fp8_quant(q, q_scale), q_scale)
+    out, lse = oracle.decode(qd, e4m3_dequantize(kc, k_scale), e4m3_dequantize(vc, v_scale),
+                             [L], bt, scale)
+    f8 = lambda x, s: float(_torch_quantize(x, s).view(torch.float8_e4m3fn).double())
+    for h in range(Hq):
+        gk = h // (Hq // Hkv)
+        s = []
+        for j in range(L):
+            acc = 0.0
+            for d in range(D):
+                acc += f8(q[0, h, d], q_scale) * f8(k[j, gk, d], k_scale)
+            s.append(scale * q_scale * k_scale * acc)
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        den = sum(w)
+        for d in range(D):
+            ref = v_scale * sum(w[j] * f8(v[j, gk, d], v_scale) for j in range(L)) / den
+            assert abs(out[0, h, d].item() - ref) < 1e-12
+        assert abs(lse[h, 0].item() - (m + math.log(den))) < 1e-12
