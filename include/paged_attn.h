@@ -36,8 +36,19 @@
  *    scalars k_scale / v_scale: the code of an element x is x / scale
  *    (fp32, correctly rounded) rounded to the nearest e4m3 value, ties to
  *    even, saturating at +-448 (NaN stays NaN); the attention reads
- *    value(code) * scale.  The query stays in dtype.  With a 16-bit cache
- *    k_scale / v_scale are ignored (may be NULL).
+ *    value(code) * scale.  With a 16-bit cache k_scale / v_scale are
+ *    ignored (may be NULL).
+ *  - q_scale (attention calls): NULL, or with an fp8 cache a device fp32
+ *    scalar that makes q an fp8 query: q then holds one-byte e4m3 codes
+ *    (same shape, e.g. from scaled_fp8_quant with this scale) and the
+ *    attention reads value(code) * q_scale [vLLM flash_attn.py (v0.9.0.1
+ *    docs), FlashAttentionImpl.forward, the fp8 branch:
+ *    ops.scaled_fp8_quant(query, layer._q_scale) and q_descale; vLLM
+ *    flash_attn.py (e2f56c3), "queries are quantized in the attention
+ *    layer"].  Every score is multiplied by q_scale * k_scale; dtype is then
+ *    the dtype of out.  q_scale with a 16-bit cache is PA_ERR_UNSUPPORTED.
+ *    With q_scale NULL an fp8 cache is attended by a 16-bit query (another
+ *    backend's option, which keeps the query unquantised).
  *  - head_size must be 64, 128 or 256; block_size a positive multiple of 16
  *    and at most 256; num_heads a multiple of num_kv_heads.
  */
@@ -146,7 +157,7 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
                        const float* alibi_slopes, const float* sinks,
                        pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
                        const float* k_scale, const float* v_scale,
-                       void* stream);
+                       const float* q_scale, void* stream);
 
 /*
  * paged_attn_decode — one query token per sequence over the paged cache,
@@ -193,7 +204,7 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
                       float softcap, const float* alibi_slopes,
                       const float* sinks, int num_splits, pa_dtype_t dtype,
                       pa_dtype_t kv_cache_dtype, const float* k_scale,
-                      const float* v_scale, void* stream);
+                      const float* v_scale, const float* q_scale, void* stream);
 
 /*
  * paged_attn_decode_noalloc — for callers that cannot allocate device
@@ -225,7 +236,8 @@ int paged_attn_decode_noalloc(void* out, float* lse, const void* q,
                               const float* alibi_slopes, const float* sinks,
                               int num_splits, pa_dtype_t dtype,
                               pa_dtype_t kv_cache_dtype, const float* k_scale,
-                              const float* v_scale, void* stream);
+                              const float* v_scale, const float* q_scale,
+                              void* stream);
 
 /*
  * merge_attn_states — combine partial attention results by their
@@ -293,7 +305,22 @@ int paged_attn_cascade(void* out, float* lse, const void* q,
                        void* parts_out, float* parts_lse,
                        int32_t* work_ints, pa_dtype_t dtype,
                        pa_dtype_t kv_cache_dtype, const float* k_scale,
-                       const float* v_scale, void* stream);
+                       const float* v_scale, const float* q_scale, void* stream);
+
+/*
+ * scaled_fp8_quant — quantise a 16-bit tensor to fp8 (e4m3) codes with a
+ * static per-tensor scale, as the attention layer does to the query when
+ * the cache is fp8 [vLLM flash_attn.py (v0.9.0.1 docs),
+ * FlashAttentionImpl.forward, ops.scaled_fp8_quant(query, layer._q_scale)].
+ *
+ *   input     num_elems elements of dtype (PA_F16 / PA_BF16), contiguous.
+ *   out       num_elems one-byte codes: out[i] = code of input[i] / *scale,
+ *             rounded as the cache codes are (see the conventions above).
+ *   scale     device fp32 scalar (the attention's q_scale / q_descale).
+ *   num_elems == 0 is a no-op.
+ */
+int scaled_fp8_quant(void* out, const void* input, const float* scale,
+                     int64_t num_elems, pa_dtype_t dtype, void* stream);
 
 /*
  * pa_local_virtual_batches — HOST-side rewriting of a batch for chunked

@@ -30,6 +30,7 @@ __all__ = [
     "paged_attn_decode",
     "paged_attn_decode_noalloc",
     "merge_attn_states",
+    "scaled_fp8_quant",
     "paged_attn_cascade",
     "local_virtual_batches",
     "check_indices",
@@ -61,22 +62,23 @@ def _load() -> ctypes.CDLL:
                                       _i32, _i32, _i32, _vp, _vp, _vp]
     lib.paged_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32,
-                                       _f32, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
+                                       _f32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
     lib.paged_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
-                                      _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+                                      _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
     lib.paged_attn_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
-                                              _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+                                              _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
     lib.merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
     lib.pa_check_indices.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i32, _vp, _vp]
     lib.paged_attn_cascade.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _vp,
-                                       _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
+                                       _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.scaled_fp8_quant.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp]
     lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
                                              _vp, _vp, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode",
-               "paged_attn_decode_noalloc", "merge_attn_states",
+               "paged_attn_decode_noalloc", "merge_attn_states", "scaled_fp8_quant",
                "pa_check_indices", "paged_attn_cascade", "pa_local_virtual_batches"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
@@ -119,6 +121,7 @@ _INT32 = (torch.int32,)
 _INT64 = (torch.int64,)
 _F32 = (torch.float32,)
 _ATTN = (torch.float16, torch.bfloat16)
+_CODES = (torch.uint8, torch.float8_e4m3fn)
 _CACHE = (torch.float16, torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
 
 
@@ -177,6 +180,16 @@ def _need_scales(k_scale, v_scale) -> None:
     _need("v_scale", v_scale, _F32, optional=True)
 
 
+def _need_q(q, out, q_scale) -> None:
+    """q in the attention dtype, or fp8 codes (uint8 / float8_e4m3fn) with
+    q_scale; out must be 16-bit and, for a 16-bit query, of the query's
+    dtype."""
+    _need("q_scale", q_scale, _F32, optional=True)
+    _need("q", q, _CODES if q_scale is not None else _ATTN, contiguous=True)
+    if q_scale is None:
+        _same_dtype("out", out, q)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -214,10 +227,11 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        lse: Optional[torch.Tensor] = None, stream=None,
                        sinks: Optional[torch.Tensor] = None,
                        k_scale: Optional[torch.Tensor] = None,
-                       v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
-    _need("q", q, _ATTN, contiguous=True)
+                       v_scale: Optional[torch.Tensor] = None,
+                       q_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_scale: q holds fp8 codes (an fp8 cache only), see the header."""
     _need("out", out, _ATTN, contiguous=True)
-    _same_dtype("out", out, q)
+    _need_q(q, out, q_scale)
     _need_cache(key_cache, value_cache)
     _need("cu_seqlens_q", cu_seqlens_q, _INT32, contiguous=True)
     _need("seq_lens", seq_lens, _INT32, contiguous=True)
@@ -234,8 +248,8 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
         _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), seq_lens.numel(), total_q,
         int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
-        int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks), _code(q.dtype),
-        _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+        int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks), _code(out.dtype),
+        _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _ptr(q_scale), _stream(stream)))
     return out
 
 
@@ -249,10 +263,13 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
                       lse: Optional[torch.Tensor] = None, stream=None,
                       sinks: Optional[torch.Tensor] = None,
                       k_scale: Optional[torch.Tensor] = None,
-                      v_scale: Optional[torch.Tensor] = None) -> None:
-    _need("q", q, _ATTN, contiguous=True)
+                      v_scale: Optional[torch.Tensor] = None,
+                      q_scale: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None) -> None:
+    """q_scale: q holds fp8 codes (an fp8 cache only); the attention dtype is
+    then out's, or out_dtype when out is None (split decode)."""
     _need("out", out, _ATTN, contiguous=True, optional=num_splits > 1)
-    _same_dtype("out", out, q)
+    _need_q(q, out, q_scale)
     _need_cache(key_cache, value_cache)
     _need("seq_lens", seq_lens, _INT32, contiguous=True)
     _need_table(block_table)
@@ -268,8 +285,19 @@ def paged_attn_decode(out: Optional[torch.Tensor], q: torch.Tensor, key_cache: t
         _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse), _ptr(q), _ptr(key_cache),
         _ptr(value_cache), _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b,
         int(max_seq_len), hq, hkv, d, bs, nb, float(scale), int(window_left), float(softcap),
-        _ptr(alibi_slopes), _ptr(sinks), int(num_splits), _code(q.dtype), _code(key_cache.dtype),
-        _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+        _ptr(alibi_slopes), _ptr(sinks), int(num_splits),
+        _code(_attn_dtype(q, out, out_dtype)), _code(key_cache.dtype), _ptr(k_scale),
+        _ptr(v_scale), _ptr(q_scale), _stream(stream)))
+
+
+def _attn_dtype(q, out, out_dtype):
+    if out is not None:
+        return out.dtype
+    if out_dtype is not None:
+        return out_dtype
+    if q.dtype in _ATTN:
+        return q.dtype
+    raise TypeError("an fp8 query without out needs out_dtype")
 
 
 def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
@@ -280,12 +308,12 @@ def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: tor
                               lse: Optional[torch.Tensor] = None, stream=None,
                               sinks: Optional[torch.Tensor] = None,
                               k_scale: Optional[torch.Tensor] = None,
-                              v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+                              v_scale: Optional[torch.Tensor] = None,
+                              q_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Split decode + merge into ``out`` with the partials in the library's
     fixed device scratch (no allocation; see the header for the limit)."""
-    _need("q", q, _ATTN, contiguous=True)
     _need("out", out, _ATTN, contiguous=True)
-    _same_dtype("out", out, q)
+    _need_q(q, out, q_scale)
     _need_cache(key_cache, value_cache)
     _need("seq_lens", seq_lens, _INT32, contiguous=True)
     _need_table(block_table)
@@ -299,8 +327,8 @@ def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: tor
         _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(seq_lens),
         _ptr(block_table), block_table.stride(0), b, int(max_seq_len), hq, hkv, d, bs, nb,
         float(scale), int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks),
-        int(num_splits), _code(q.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale),
-        _stream(stream)))
+        int(num_splits), _code(out.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale),
+        _ptr(q_scale), _stream(stream)))
     return out
 
 
@@ -326,14 +354,14 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        max_prefix_splits: int = 16, workspace=None, stream=None,
                        sinks: Optional[torch.Tensor] = None,
                        k_scale: Optional[torch.Tensor] = None,
-                       v_scale: Optional[torch.Tensor] = None) -> None:
+                       v_scale: Optional[torch.Tensor] = None,
+                       q_scale: Optional[torch.Tensor] = None) -> None:
     """Causal prefill over a shared prefix (see paged_attn_cascade in the
     header).  ``workspace`` is (parts_out, parts_lse, work_ints) sized for
     max_prefix_splits + 1 parts; it is allocated here with torch when not
     given."""
-    _need("q", q, _ATTN, contiguous=True)
     _need("out", out, _ATTN, contiguous=True)
-    _same_dtype("out", out, q)
+    _need_q(q, out, q_scale)
     _need_cache(key_cache, value_cache)
     _need("cu_seqlens_q", cu_seqlens_q, _INT32, contiguous=True)
     _need("seq_lens", seq_lens, _INT32, contiguous=True)
@@ -346,11 +374,11 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
     b = seq_lens.numel()
     if workspace is None:
         n = max_prefix_splits + 1
-        workspace = (torch.empty(n, t, hq, d, dtype=q.dtype, device=q.device),
+        workspace = (torch.empty(n, t, hq, d, dtype=out.dtype, device=q.device),
                      torch.empty(n, hq, t, dtype=torch.float32, device=q.device),
                      torch.empty(b + 3, dtype=torch.int32, device=q.device))
     parts_out, parts_lse, ints = workspace
-    _need("workspace parts_out", parts_out, (q.dtype,), contiguous=True)
+    _need("workspace parts_out", parts_out, (out.dtype,), contiguous=True)
     _need("workspace parts_lse", parts_lse, _F32, contiguous=True)
     _need("workspace ints", ints, _INT32, contiguous=True)
     _check("paged_attn_cascade", lib.paged_attn_cascade(
@@ -358,7 +386,22 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b, t, int(max_seqlen_q),
         int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), float(softcap), _ptr(sinks),
         int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), _ptr(ints),
-        _code(q.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+        _code(out.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _ptr(q_scale),
+        _stream(stream)))
+
+
+def scaled_fp8_quant(out: torch.Tensor, input: torch.Tensor, scale: torch.Tensor,
+                     stream=None) -> torch.Tensor:
+    """fp8 (e4m3) codes of input / scale into ``out`` (uint8 or
+    float8_e4m3fn, same number of elements); scale a device fp32 scalar."""
+    _need("input", input, _ATTN, contiguous=True)
+    _need("out", out, _CODES, contiguous=True)
+    _need("scale", scale, _F32)
+    if out.numel() != input.numel():
+        raise ValueError("out and input must hold the same number of elements")
+    _check("scaled_fp8_quant", lib.scaled_fp8_quant(
+        _ptr(out), _ptr(input), _ptr(scale), input.numel(), _code(input.dtype), _stream(stream)))
+    return out
 
 
 def local_virtual_batches(attn_chunk_size: int, query_start_loc, seq_lens, block_table,

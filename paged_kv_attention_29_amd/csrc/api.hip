@@ -99,12 +99,21 @@ int check_kv(const char* fn, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype, const 
   return PA_OK;
 }
 
+// An fp8 query (q_scale non-null: q holds e4m3 codes, q_scale their
+// descale) comes with an fp8 cache, as on the pages: the query is quantised
+// only when the cache is.
+int check_q8(const char* fn, pa_dtype_t kv_cache_dtype, const float* q_scale) {
+  if (q_scale != nullptr && kv_cache_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "%s: an fp8 query (q_scale) needs an fp8 cache", fn);
+  return PA_OK;
+}
+
 // Checks shared by the decode entry points (paged_attn_decode and its
 // no-allocation variant).
 int check_decode(const char* fn, int num_seqs, int max_seq_len, int num_heads, int num_kv_heads,
                  int head_size, int block_size, int64_t num_blocks, float scale, int window_left,
                  float softcap, int num_splits, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
-                 const float* k_scale, const float* v_scale, const void* q,
+                 const float* k_scale, const float* v_scale, const float* q_scale, const void* q,
                  const void* key_cache, const void* value_cache, const int32_t* seq_lens,
                  const int32_t* block_table, int64_t block_table_stride) {
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
@@ -112,6 +121,8 @@ int check_decode(const char* fn, int num_seqs, int max_seq_len, int num_heads, i
                              value_cache, seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
   rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
+  if (rc != PA_OK) return rc;
+  rc = check_q8(fn, kv_cache_dtype, q_scale);
   if (rc != PA_OK) return rc;
   if (num_splits < 1 || num_splits > 256)
     return fail(PA_ERR_INVALID, "%s: num_splits must be in [1, 256] (got %d)", fn, num_splits);
@@ -131,7 +142,7 @@ pa::AttnParams decode_params(void* out, float* lse, float* part_out, float* part
                              float scale, int window_left, float softcap,
                              const float* alibi_slopes, const float* sinks, int num_splits,
                              pa_dtype_t dtype, pa_dtype_t kv_cache_dtype, const float* k_scale,
-                             const float* v_scale) {
+                             const float* v_scale, const float* q_scale) {
   pa::AttnParams p{};
   p.out = out;
   p.lse = lse;
@@ -162,6 +173,7 @@ pa::AttnParams decode_params(void* out, float* lse, float* part_out, float* part
   p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.q_scale = q_scale;
   return p;
 }
 
@@ -214,13 +226,16 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
                        int head_size, int block_size, int64_t num_blocks, float scale, int causal,
                        int window_left, float softcap, const float* alibi_slopes,
                        const float* sinks, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
-                       const float* k_scale, const float* v_scale, void* stream) {
+                       const float* k_scale, const float* v_scale, const float* q_scale,
+                       void* stream) {
   const char* fn = "paged_attn_prefill";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, window_left, softcap, dtype, q, key_cache,
                              value_cache, seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
   rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
+  if (rc != PA_OK) return rc;
+  rc = check_q8(fn, kv_cache_dtype, q_scale);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -265,6 +280,7 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
   p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.q_scale = q_scale;
   return hip_result(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -275,12 +291,13 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
                       int block_size, int64_t num_blocks, float scale, int window_left,
                       float softcap, const float* alibi_slopes, const float* sinks,
                       int num_splits, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
-                      const float* k_scale, const float* v_scale, void* stream) {
+                      const float* k_scale, const float* v_scale, const float* q_scale,
+                      void* stream) {
   const char* fn = "paged_attn_decode";
   int rc = check_decode(fn, num_seqs, max_seq_len, num_heads, num_kv_heads, head_size, block_size,
                         num_blocks, scale, window_left, softcap, num_splits, dtype,
-                        kv_cache_dtype, k_scale, v_scale, q, key_cache, value_cache, seq_lens,
-                        block_table, block_table_stride);
+                        kv_cache_dtype, k_scale, v_scale, q_scale, q, key_cache, value_cache,
+                        seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
   if (num_splits == 1 && out == nullptr)
     return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
@@ -291,7 +308,7 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
                                    seq_lens, block_table, block_table_stride, num_seqs,
                                    max_seq_len, num_heads, num_kv_heads, head_size, block_size,
                                    scale, window_left, softcap, alibi_slopes, sinks, num_splits,
-                                   dtype, kv_cache_dtype, k_scale, v_scale);
+                                   dtype, kv_cache_dtype, k_scale, v_scale, q_scale);
   return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -303,12 +320,12 @@ int paged_attn_decode_noalloc(void* out, float* lse, const void* q, const void* 
                               int window_left, float softcap, const float* alibi_slopes,
                               const float* sinks, int num_splits, pa_dtype_t dtype,
                               pa_dtype_t kv_cache_dtype, const float* k_scale,
-                              const float* v_scale, void* stream) {
+                              const float* v_scale, const float* q_scale, void* stream) {
   const char* fn = "paged_attn_decode_noalloc";
   int rc = check_decode(fn, num_seqs, max_seq_len, num_heads, num_kv_heads, head_size, block_size,
                         num_blocks, scale, window_left, softcap, num_splits, dtype,
-                        kv_cache_dtype, k_scale, v_scale, q, key_cache, value_cache, seq_lens,
-                        block_table, block_table_stride);
+                        kv_cache_dtype, k_scale, v_scale, q_scale, q, key_cache, value_cache,
+                        seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   // partial results [S, B, Hq, D] fp32, then their LSEs [S, Hq, B] at a
@@ -338,7 +355,7 @@ int paged_attn_decode_noalloc(void* out, float* lse, const void* q, const void* 
                                    block_table, block_table_stride, num_seqs, max_seq_len,
                                    num_heads, num_kv_heads, head_size, block_size, scale,
                                    window_left, softcap, alibi_slopes, sinks, num_splits, dtype,
-                                   kv_cache_dtype, k_scale, v_scale);
+                                   kv_cache_dtype, k_scale, v_scale, q_scale);
   rc = pa::launch_decode(p, st);
   if (rc == 0 && num_splits > 1)
     rc = pa::launch_merge(out, lse, part_out, part_lse, num_splits, num_seqs, num_heads,
@@ -379,13 +396,15 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
                        int max_prefix_splits,
                        void* parts_out, float* parts_lse, int32_t* work_ints, pa_dtype_t dtype,
                        pa_dtype_t kv_cache_dtype, const float* k_scale, const float* v_scale,
-                       void* stream) {
+                       const float* q_scale, void* stream) {
   const char* fn = "paged_attn_cascade";
   int rc = check_attn_common(fn, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              num_blocks, scale, -1, softcap, dtype, q, key_cache, value_cache,
                              seq_lens, block_table, block_table_stride);
   if (rc != PA_OK) return rc;
   rc = check_kv(fn, dtype, kv_cache_dtype, k_scale, v_scale, true);
+  if (rc != PA_OK) return rc;
+  rc = check_q8(fn, kv_cache_dtype, q_scale);
   if (rc != PA_OK) return rc;
   if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -442,8 +461,24 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
   p.kv_fp8 = kv_cache_dtype == PA_FP8_E4M3;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.q_scale = q_scale;
   return hip_result(pa::launch_cascade(p, common_prefix_len, max_prefix_splits, parts_out,
                                        parts_lse, work_ints, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int scaled_fp8_quant(void* out, const void* input, const float* scale, int64_t num_elems,
+                     pa_dtype_t dtype, void* stream) {
+  const char* fn = "scaled_fp8_quant";
+  if (!is_16bit(dtype))
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_F16 or PA_BF16 (got %d)", fn, (int)dtype);
+  if (num_elems < 0) return fail(PA_ERR_INVALID, "%s: num_elems must be >= 0", fn);
+  if (num_elems > 0 && (out == nullptr || input == nullptr || scale == nullptr))
+    return fail(PA_ERR_INVALID, "%s: NULL out, input or scale", fn);
+  if (num_elems == 0) return ok();
+  return hip_result(pa::launch_scaled_fp8_quant(out, input, scale, num_elems,
+                                                static_cast<pa::Dtype>(dtype),
+                                                static_cast<hipStream_t>(stream)),
                     fn);
 }
 

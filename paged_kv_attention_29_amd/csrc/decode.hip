@@ -61,9 +61,12 @@ struct DecodeArgs {
   // are the K / V values); null for a 16-bit cache
   const float* k_scale;
   const float* v_scale;
+  // fp8 query (with an fp8 cache): q holds e4m3 codes and this device fp32
+  // scalar is their descale; null for a 16-bit query
+  const float* q_scale;
 };
 
-enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4 };
+enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4, kQ8 = 8 };
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // A work item covers HPW adjacent KV heads (2 when the head counts allow it
@@ -238,6 +241,7 @@ struct Dec {
   static constexpr bool SOFTCAP = FEAT & kSoftcap;
   static constexpr bool ALIBI = FEAT & kAlibi;
   static constexpr bool F8 = FEAT & kFp8;
+  static constexpr bool Q8 = FEAT & kQ8;  // fp8 query codes (widened exactly to T)
   static constexpr int KK = D / 32;   // QK mfma steps along D
   static constexpr int NU = D / 64;   // fp8: 16-byte pieces of a row per lane
   static constexpr int DC = D / 16;   // PV output chunks of 16 rows of D
@@ -361,24 +365,42 @@ struct Dec {
   }
 
   // The Q row of this lane's column (head g0 * G + r16; padding columns load
-  // the item's first head and are masked by mask_q), without a branch.
+  // the item's first head and are masked by mask_q), without a branch.  An
+  // fp8 query is loaded as its codes (8 bytes per step) and widened in
+  // mask_q, after the wait for the first K/V step.
+  using QRaw = std::conditional_t<Q8, u32x2, v8s>;
   static __device__ __forceinline__ void load_q(const DecodeArgs& a, const Item& it, int r16,
-                                                int c4, v8s (&qraw)[KK]) {
+                                                int c4, QRaw (&qraw)[KK]) {
     const int hq = it.g0 * a.G + (r16 < a.G * HPW ? r16 : 0);
-    const uint16_t* qrow = a.q + ((int64_t)it.b * a.Hq + hq) * D;
+    if constexpr (Q8) {
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)it.b * a.Hq + hq) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const v8s*>(qrow + qk_off(kk, c4));
+      for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x2*>(qrow + qk_off(kk, c4));
+    } else {
+      const uint16_t* qrow = a.q + ((int64_t)it.b * a.Hq + hq) * D;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const v8s*>(qrow + qk_off(kk, c4));
+    }
+  }
+  static __device__ __forceinline__ v8s q_elems(const QRaw& r) {
+    if constexpr (Q8) {
+      const v4s lo = T::from_fp8x4(r[0]), hi = T::from_fp8x4(r[1]);
+      return v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return r;
+    }
   }
   // Q^T as the B operand: column r16, D elements kk*32 + c4*8 .. +8; with two
   // KV heads, operand h is zero outside head h's columns, so the two products
   // accumulate into one S^T tile
-  static __device__ __forceinline__ void mask_q(const v8s (&qraw)[KK], bool col_ok, int hsel,
+  static __device__ __forceinline__ void mask_q(const QRaw (&qraw)[KK], bool col_ok, int hsel,
                                                 v8s (&qf)[HPW][KK]) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+      const v8s qv = q_elems(qraw[kk]);
 #pragma unroll
-      for (int h = 0; h < HPW; ++h) qf[h][kk] = (col_ok && hsel == h) ? qraw[kk] : z;
+      for (int h = 0; h < HPW; ++h) qf[h][kk] = (col_ok && hsel == h) ? qv : z;
     }
   }
   // ALiBi slope of this lane's column, in log2 units
@@ -609,6 +631,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
     a.scale_log2 *= ks;
     a.cap_k2 *= ks;
   }
+  if constexpr (K::Q8) {
+    // and so does an fp8 query's descale
+    const float qs = *a.q_scale;
+    a.scale_log2 *= qs;
+    a.cap_k2 *= qs;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -645,7 +673,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int hsel = r16 / a.G;  // which of the item's KV heads the column reads
   const float slope_log2 = K::slope_of(a, it, r16);
 
-  v8s qraw[K::KK];
+  typename K::QRaw qraw[K::KK];
   K::load_q(a, it, r16, c4, qraw);
 
   float m_run = kNegInf;
@@ -764,7 +792,12 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.sinks = p.sinks;
   a.k_scale = p.k_scale;
   a.v_scale = p.v_scale;
+  a.q_scale = p.q_scale;
   const bool alibi = p.alibi_slopes != nullptr;
+  if (p.kv_fp8 && p.q_scale != nullptr) {
+    if (p.dtype == kBF16) return launch_t<BF16, kFp8 | kQ8>(a, p.head_size, softcap, alibi, stream);
+    return launch_t<F16, kFp8 | kQ8>(a, p.head_size, softcap, alibi, stream);
+  }
   if (p.kv_fp8) {
     if (p.dtype == kBF16) return launch_t<BF16, kFp8>(a, p.head_size, softcap, alibi, stream);
     return launch_t<F16, kFp8>(a, p.head_size, softcap, alibi, stream);

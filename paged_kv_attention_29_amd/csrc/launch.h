@@ -21,6 +21,10 @@ int launch_reshape_and_cache_fp8(const void* key, const void* value, int64_t key
                                  Dtype in_dtype, const float* k_scale, const float* v_scale,
                                  hipStream_t stream);
 
+// the query quantiser: out[i] = e4m3 code of input[i] / *scale
+int launch_scaled_fp8_quant(void* out, const void* input, const float* scale, int64_t n,
+                            Dtype in_dtype, hipStream_t stream);
+
 int launch_merge(void* out, float* out_lse, const void* parts, const float* parts_lse,
                  int num_parts, int64_t num_tokens, int num_heads, int head_size,
                  Dtype parts_dtype, Dtype out_dtype, hipStream_t stream);
@@ -54,6 +58,7 @@ struct AttnParams {
   int kv_fp8;          // nonzero: the caches hold fp8 (e4m3) codes
   const float* k_scale;  // fp8 cache: device fp32 scales
   const float* v_scale;
+  const float* q_scale;  // non-null: q holds fp8 (e4m3) codes and this is their descale
   int num_splits;
   int key_split;  // prefill only: keys per split (a multiple of 64), 0 = none
   Dtype dtype;

@@ -46,7 +46,7 @@ namespace {
 constexpr int kKT = 64;       // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4 };
+enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4, kQ8 = 8 };
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -80,6 +80,9 @@ struct PrefillArgs {
   // the K / V value); null for a 16-bit cache
   const float* k_scale;
   const float* v_scale;
+  // fp8 query (with an fp8 cache): q holds e4m3 codes and this device fp32
+  // scalar is their descale; null for a 16-bit query
+  const float* q_scale;
 };
 
 // Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
@@ -152,6 +155,12 @@ __device__ __forceinline__ v8s load16_async(const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p));
   return r;
 }
+// 8-byte global load the compiler does not track (same contract)
+__device__ __forceinline__ u32x2 load8_async(const void* p) {
+  u32x2 r;
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p));
+  return r;
+}
 // 4-byte global load the compiler does not track (same contract)
 __device__ __forceinline__ uint32_t load4_async(const void* p) {
   uint32_t r;
@@ -161,6 +170,7 @@ __device__ __forceinline__ uint32_t load4_async(const void* p) {
 // orders every use of r after the preceding (explicit) wait
 __device__ __forceinline__ void claim(v8s& r) { asm volatile("" : "+v"(r)); }
 __device__ __forceinline__ void claim(uint32_t& r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void claim(u32x2& r) { asm volatile("" : "+v"(r)); }
 
 // max of v over lanes l and l ^ 32 (v_permlane32_swap exchanges the halves)
 __device__ __forceinline__ float swap_halves_max(float v) {
@@ -192,6 +202,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
   constexpr bool F8 = FEAT & kFp8;
+  constexpr bool Q8 = FEAT & kQ8;  // fp8 query codes (widened exactly to T)
   constexpr int NW = kNW<D>;
   constexpr int NST = kNST<D>;
   constexpr int TB = kTileBytes<D>;
@@ -218,6 +229,12 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     a.scale_log2 *= ks;
     a.cap_k2 *= ks;
     v_scale = *a.v_scale;
+  }
+  if constexpr (Q8) {
+    // an fp8 query's descale multiplies every score too
+    const float qs = *a.q_scale;
+    a.scale_log2 *= qs;
+    a.cap_k2 *= qs;
   }
 
   // Grid (Hkv * query tiles, sequences), x = tile' * Hkv + g.  Workgroups are
@@ -287,11 +304,19 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   // also counts the DMAs in flight.  They complete before the prologue's
   // DMA wait (loads complete in order) and are claimed after it.
   v8s qf[KQ];
+  u32x2 q8[Q8 ? KQ : 1];  // an fp8 query's codes, widened after the wait
   {
     const int64_t qtok = row_ok ? q0 + tok0 + tk : q0;  // rows past the tile read a valid row
-    const uint16_t* qrow = a.q + (qtok * a.Hq + head) * D + 8 * g2;
+    if constexpr (Q8) {
+      const uint8_t* qrow =
+          reinterpret_cast<const uint8_t*>(a.q) + (qtok * a.Hq + head) * D + 8 * g2;
 #pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) qf[kk] = load16_async(qrow + 16 * kk);
+      for (int kk = 0; kk < KQ; ++kk) q8[kk] = load8_async(qrow + 16 * kk);
+    } else {
+      const uint16_t* qrow = a.q + (qtok * a.Hq + head) * D + 8 * g2;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) qf[kk] = load16_async(qrow + 16 * kk);
+    }
   }
   wait_vmcnt<KQ>();  // the block ids (issued before Q) landed
   claim(ids);
@@ -586,7 +611,13 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   lds_barrier();
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk) {
-    claim(qf[kk]);
+    if constexpr (Q8) {
+      claim(q8[kk]);
+      const v4s lo = T::from_fp8x4(q8[kk][0]), hi = T::from_fp8x4(q8[kk][1]);
+      qf[kk] = v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      claim(qf[kk]);
+    }
     const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
     if (!row_ok) qf[kk] = z;
   }
@@ -755,8 +786,14 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.sinks = p.sinks;
   a.k_scale = p.k_scale;
   a.v_scale = p.v_scale;
+  a.q_scale = p.q_scale;
   const int ns = p.key_split > 0 ? (p.max_seqlen_k + p.key_split - 1) / p.key_split : 1;
   const bool alibi = p.alibi_slopes != nullptr;
+  if (p.kv_fp8 && p.q_scale != nullptr) {
+    if (p.dtype == kBF16)
+      return launch_t<BF16, kFp8 | kQ8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+    return launch_t<F16, kFp8 | kQ8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+  }
   if (p.kv_fp8) {
     if (p.dtype == kBF16)
       return launch_t<BF16, kFp8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);

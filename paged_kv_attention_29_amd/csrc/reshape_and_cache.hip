@@ -152,6 +152,51 @@ int launch_reshape_and_cache_fp8(const void* key, const void* value, int64_t key
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// The query quantiser (scaled_fp8_quant with a static per-tensor scale; vLLM
+// flash_attn.py (v0.9.0.1 docs), FlashAttentionImpl.forward, the fp8
+// branch): each element divided by the scale, then e4m3_code, as for the
+// cache.  VEC consecutive elements per lane, grid-stride.
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void scaled_fp8_quant_kernel(const uint16_t* __restrict__ in,
+                                                               uint8_t* __restrict__ out,
+                                                               const float* __restrict__ scale,
+                                                               int64_t n_vec) {
+  typedef uint16_t in_t __attribute__((ext_vector_type(VEC)));
+  const float s = *scale;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const in_t x = reinterpret_cast<const in_t*>(in)[i];
+    if constexpr (VEC == 8) {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_code(T::to_float(x[e]) / s) << (8 * (e & 3));
+      reinterpret_cast<u32x2*>(out)[i] = u32x2{w[0], w[1]};
+    } else {
+      out[i] = static_cast<uint8_t>(e4m3_code(T::to_float(x[0]) / s));
+    }
+  }
+}
+
+int launch_scaled_fp8_quant(void* out, const void* input, const float* scale, int64_t n,
+                            Dtype in_dtype, hipStream_t stream) {
+  const bool aligned = n % 8 == 0 && reinterpret_cast<uintptr_t>(input) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(out) % 8 == 0;
+  const int64_t n_vec = aligned ? n / 8 : n;
+  int64_t blocks = (n_vec + 255) / 256;
+  if (blocks > (1 << 16)) blocks = 1 << 16;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const uint16_t* in = static_cast<const uint16_t*>(input);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  if (in_dtype == kBF16) {
+    if (aligned) hipLaunchKernelGGL((scaled_fp8_quant_kernel<BF16, 8>), grid, block, 0, stream, in, o, scale, n_vec);
+    else hipLaunchKernelGGL((scaled_fp8_quant_kernel<BF16, 1>), grid, block, 0, stream, in, o, scale, n_vec);
+  } else {
+    if (aligned) hipLaunchKernelGGL((scaled_fp8_quant_kernel<F16, 8>), grid, block, 0, stream, in, o, scale, n_vec);
+    else hipLaunchKernelGGL((scaled_fp8_quant_kernel<F16, 1>), grid, block, 0, stream, in, o, scale, n_vec);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 int launch_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
                              int64_t value_stride, void* key_cache, void* value_cache,
                              const int64_t* slots, int64_t num_tokens, int row_elems,

@@ -59,7 +59,7 @@ def _decode(pa, **kw):
     args = dict(out=1, lse=None, part_out=None, part_lse=None, q=1, kc=1, vc=1, seq_lens=1,
                 bt=1, bt_stride=4, num_seqs=2, max_seq_len=10, hq=4, hkv=2, d=64, bs=16, nb=8,
                 scale=0.125, wl=-1, cap=0.0, alibi=None, sinks=None, splits=1, dtype=pa.PA_F16,
-                kvdt=pa.PA_F16, ks=None, vs=None)
+                kvdt=pa.PA_F16, ks=None, vs=None, qs=None)
     args.update(kw)
     return pa.lib.paged_attn_decode(*args.values(), None)
 
@@ -68,7 +68,7 @@ def _prefill(pa, **kw):
     args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
                 num_seqs=1, total_q=5, mq=5, mk=23, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
                 causal=1, wl=-1, cap=0.0, alibi=None, sinks=None, dtype=pa.PA_F16,
-                kvdt=pa.PA_F16, ks=None, vs=None)
+                kvdt=pa.PA_F16, ks=None, vs=None, qs=None)
     args.update(kw)
     return pa.lib.paged_attn_prefill(*args.values(), None)
 
@@ -105,6 +105,24 @@ def test_fp8_cache_validation(lib):
     assert _prefill(lib, kvdt=9, ks=1, vs=1) == -2
     assert _cascade(lib, kvdt=F8, ks=1, vs=None) == -1
     assert lib.pa_last_error().startswith("paged_attn_cascade")
+
+
+def test_fp8_query_needs_an_fp8_cache(lib):
+    F8 = lib.PA_FP8_E4M3
+    assert _decode(lib, qs=1) == -2 and "fp8 cache" in lib.pa_last_error()
+    assert _prefill(lib, qs=1) == -2
+    assert _cascade(lib, qs=1) == -2
+    # with an fp8 cache the fp8 query passes validation; q = NULL then fails
+    assert _decode(lib, kvdt=F8, ks=1, vs=1, qs=1, q=None) == -1
+
+
+def test_scaled_fp8_quant_validation(lib):
+    f = lib.lib.scaled_fp8_quant
+    assert f(16, 16, 16, 8, lib.PA_F32, None) == -2            # 16-bit input only
+    assert f(16, 16, 16, -1, lib.PA_BF16, None) == -1
+    assert f(None, 16, 16, 8, lib.PA_BF16, None) == -1
+    assert f(16, 16, None, 8, lib.PA_BF16, None) == -1
+    assert f(None, None, None, 0, lib.PA_BF16, None) == 0      # empty: no-op
 
 
 def test_empty_calls_are_noops(lib):
@@ -157,7 +175,7 @@ def _cascade(pa, **kw):
     args = dict(out=1, lse=None, q=1, kc=1, vc=1, cu=1, seq_lens=1, bt=1, bt_stride=4,
                 num_seqs=2, total_q=5, mq=3, mk=80, hq=4, hkv=2, d=64, bs=16, nb=8, scale=0.125,
                 cap=0.0, sinks=None, prefix=32, max_splits=4, parts=1, parts_lse=1, ints=1, dtype=pa.PA_BF16,
-                kvdt=pa.PA_BF16, ks=None, vs=None)
+                kvdt=pa.PA_BF16, ks=None, vs=None, qs=None)
     args.update(kw)
     return pa.lib.paged_attn_cascade(*args.values(), None)
 

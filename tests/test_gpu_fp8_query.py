@@ -1,0 +1,164 @@
+"""GPU parity of the fp8-query path: the query quantiser (scaled_fp8_quant)
+bit for bit against the oracle's, and decode / prefill / cascade / the
+no-allocation decode with an fp8 query (q_scale) over an fp8 cache against
+the oracle attending the dequantised query and cache.  The oracle quantises
+the query itself (its codes never come from the GPU)."""
+import pytest
+import torch
+
+import oracle
+from oracle.fp8 import dequantize_query, e4m3_dequantize, scaled_fp8_quant
+from oracle_side import assert_attn_close, assert_lse_close
+from test_gpu_fp8 import DECODE, PREFILL, _fp8_cache
+
+pytestmark = pytest.mark.gpu
+
+Q_SCALE = 2.6 / 448.0   # the largest |q| of the 0.5 * N(0,1) queries maps near 448
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_attention_29_amd as pa
+    return pa
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("n,offset", [(4096 * 8, 0), (1001, 0), (800, 3)])
+def test_scaled_fp8_quant_bitexact(pa, dtype, n, offset):
+    print(f"\n[gpu-case] scaled_fp8_quant n={n} offset={offset} {dtype}", flush=True)
+    g = torch.Generator().manual_seed(n + offset)
+    x = (torch.randn(n + offset, generator=g) * 3).to(dtype)
+    x[offset:offset + 6] = torch.tensor([float("inf"), -float("inf"), float("nan"), -0.0, 1e4,
+                                         3e-6]).to(dtype)
+    for scale in (0.0125, 2.6 / 448.0):
+        xd = x.cuda()[offset:]
+        out = torch.full((n,), 0xAA, dtype=torch.uint8, device="cuda")
+        pa.scaled_fp8_quant(out, xd, torch.tensor([scale], device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), scaled_fp8_quant(x[offset:], scale))
+
+
+def _quantised_query(pa, q):
+    qd = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+    pa.scaled_fp8_quant(qd, q.cuda(), torch.tensor([Q_SCALE], device="cuda"))
+    return qd
+
+
+def _dequantised(kc, vc, k_scale, v_scale):
+    kf, vf = e4m3_dequantize(kc, k_scale), e4m3_dequantize(vc, v_scale)
+    kf[torch.isnan(kf)] = 0.0                  # (the spare block is never visible)
+    vf[torch.isnan(vf)] = 0.0
+    return kf, vf
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
+def test_decode_fp8_query(pa, case):
+    name, lens, Hq, Hkv, D, bs, dtype, wl, cap, alibi, sinks, S = case
+    print(f"\n[gpu-case] decode fp8 query {name}", flush=True)
+    seed = len(name) * 7
+    k_scale, v_scale = 0.011, 0.0075
+    kc, vc, table = _fp8_cache(seed, lens, Hkv, D, bs, k_scale, v_scale)
+    g = torch.Generator().manual_seed(seed + 1)
+    B = len(lens)
+    q = (torch.randn(B, Hq, D, generator=g) * 0.5).to(dtype)
+    slopes = torch.rand(Hq, generator=g) * 0.05 if alibi else None
+    sk = torch.randn(Hq, generator=g) if sinks else None
+    scale = D ** -0.5
+    dev = lambda t: None if t is None else t.cuda()
+    kw = dict(k_scale=torch.tensor([k_scale], device="cuda"),
+              v_scale=torch.tensor([v_scale], device="cuda"),
+              q_scale=torch.tensor([Q_SCALE], device="cuda"), sinks=dev(sk))
+    q8 = _quantised_query(pa, q)
+    kcd, vcd, td = kc.cuda(), vc.cuda(), table.cuda()
+    lensd = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.full((B, Hq, D), float("nan"), dtype=dtype, device="cuda")
+    lse = torch.full((Hq, B), float("nan"), device="cuda")
+    if S == 1:
+        pa.paged_attn_decode(out, q8, kcd, vcd, lensd, td, max(lens), scale, wl, cap,
+                             dev(slopes), lse=lse, **kw)
+    else:
+        po = torch.full((S, B, Hq, D), float("nan"), device="cuda")
+        pl = torch.full((S, Hq, B), float("nan"), device="cuda")
+        pa.paged_attn_decode(None, q8, kcd, vcd, lensd, td, max(lens), scale, wl, cap,
+                             dev(slopes), S, part_out=po, part_lse=pl, out_dtype=dtype, **kw)
+        pa.merge_attn_states(out, po, pl, out_lse=lse)
+    # the no-allocation decode takes the same fp8 query
+    out_na = torch.full_like(out, float("nan"))
+    lse_na = torch.full_like(lse, float("nan"))
+    pa.paged_attn_decode_noalloc(out_na, q8, kcd, vcd, lensd, td, max(lens), scale, wl, cap,
+                                 dev(slopes), S, lse=lse_na, **kw)
+    torch.cuda.synchronize()
+    kf, vf = _dequantised(kc, vc, k_scale, v_scale)
+    qf = dequantize_query(scaled_fp8_quant(q, Q_SCALE), Q_SCALE)
+    ro, rl = oracle.decode(qf, kf, vf, lens, table, scale, wl, cap, slopes, sinks=sk)
+    assert_attn_close(out, ro, name)
+    assert_lse_close(lse, rl, f"{name} lse")
+    assert torch.equal(out_na.view(torch.int16), out.view(torch.int16)), f"{name} noalloc"
+    assert torch.equal(lse_na, lse), f"{name} noalloc lse"
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
+def test_prefill_fp8_query(pa, case):
+    name, ctx, q_lens, Hq, Hkv, D, bs, dtype, causal, wl, cap, alibi, sinks = case
+    print(f"\n[gpu-case] prefill fp8 query {name}", flush=True)
+    seed = len(name) * 11
+    k_scale, v_scale = 0.011, 0.0075
+    lens = [c + n for c, n in zip(ctx, q_lens)]
+    kc, vc, table = _fp8_cache(seed, lens, Hkv, D, bs, k_scale, v_scale)
+    g = torch.Generator().manual_seed(seed + 1)
+    cu = [0]
+    for n in q_lens:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    q = (torch.randn(T, Hq, D, generator=g) * 0.5).to(dtype)
+    slopes = torch.rand(Hq, generator=g) * 0.05 if alibi else None
+    sk = torch.randn(Hq, generator=g) if sinks else None
+    scale = D ** -0.5
+    dev = lambda t: None if t is None else t.cuda()
+    out = torch.full((T, Hq, D), float("nan"), dtype=dtype, device="cuda")
+    lse = torch.full((Hq, T), float("nan"), device="cuda")
+    pa.paged_attn_prefill(out, _quantised_query(pa, q), kc.cuda(), vc.cuda(),
+                          torch.tensor(cu, dtype=torch.int32, device="cuda"),
+                          torch.tensor(lens, dtype=torch.int32, device="cuda"), table.cuda(),
+                          max(q_lens), max(lens), scale, causal, wl, cap, dev(slopes), lse=lse,
+                          sinks=dev(sk), k_scale=torch.tensor([k_scale], device="cuda"),
+                          v_scale=torch.tensor([v_scale], device="cuda"),
+                          q_scale=torch.tensor([Q_SCALE], device="cuda"))
+    torch.cuda.synchronize()
+    kf, vf = _dequantised(kc, vc, k_scale, v_scale)
+    qf = dequantize_query(scaled_fp8_quant(q, Q_SCALE), Q_SCALE)
+    ro, rl = oracle.attend(qf, kf, vf, cu, lens, table, scale, causal, wl, cap, slopes, sinks=sk)
+    assert_attn_close(out, ro, name)
+    assert_lse_close(lse, rl, f"{name} lse")
+
+
+def test_cascade_fp8_query(pa):
+    from oracle.fp8 import e4m3_quantize
+    from test_gpu_cascade import _case
+    print("\n[gpu-case] cascade fp8 query", flush=True)
+    prefix, q_lens, extra = 256, [1, 37, 64, 1, 129], [0, 100, 7, 300, 64]
+    Hq, Hkv, D, bs = 32, 8, 128, 16
+    q, kc, vc, cu, lens, table = _case(43, prefix, q_lens, extra, Hq, Hkv, D, bs, torch.bfloat16)
+    q = (q.float() * 0.5).to(torch.bfloat16)
+    k_scale, v_scale = 0.011, 0.0075
+    kc8, vc8 = e4m3_quantize(kc, k_scale), e4m3_quantize(vc, v_scale)
+    scale = D ** -0.5
+    T = cu[-1]
+    kw = dict(k_scale=torch.tensor([k_scale], device="cuda"),
+              v_scale=torch.tensor([v_scale], device="cuda"),
+              q_scale=torch.tensor([Q_SCALE], device="cuda"))
+    cud = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    lensd = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q8, kd, vd, td = _quantised_query(pa, q), kc8.cuda(), vc8.cuda(), table.cuda()
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Hq, T), float("nan"), device="cuda")
+    pa.paged_attn_cascade(out, q8, kd, vd, cud, lensd, td, max(q_lens), max(lens), scale, prefix,
+                          lse=lse, **kw)
+    torch.cuda.synchronize()
+    kf, vf = _dequantised(kc8, vc8, k_scale, v_scale)
+    qf = dequantize_query(scaled_fp8_quant(q, Q_SCALE), Q_SCALE)
+    ro, rl = oracle.cascade(qf, kf, vf, cu, lens, table, scale, prefix)
+    assert_attn_close(out, ro, "cascade fp8 query")
+    assert_lse_close(lse, rl, "cascade fp8 query lse")

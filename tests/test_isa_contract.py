@@ -79,7 +79,7 @@ def test_untracked_load_results_are_not_touched_before_their_wait(prefill_asm):
                 pending = [(o, d) for (o, d) in pending
                            if sum(1 for (o2, _) in pending if o2 > o) < n]
                 continue
-            if in_asm and op in ("global_load_dwordx4", "global_load_dword"):
+            if in_asm and op in ("global_load_dwordx4", "global_load_dwordx2", "global_load_dword"):
                 pending.append((order, _vregs(l.split()[1].rstrip(","))))
                 order += 1
                 checked += 1

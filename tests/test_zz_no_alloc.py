@@ -35,7 +35,7 @@ def _existing_and_noalloc(pa, runner, w, S):
         w.head_size, w.block_size, w.num_blocks, w.scale, w.window_left, w.softcap,
         None if cache.alibi is None else cache.alibi.data_ptr(), None, S,
         pa.PA_BF16 if w.dtype == torch.bfloat16 else pa.PA_F16,
-        pa.PA_BF16 if w.dtype == torch.bfloat16 else pa.PA_F16, None, None,
+        pa.PA_BF16 if w.dtype == torch.bfloat16 else pa.PA_F16, None, None, None,
         torch.cuda.current_stream().cuda_stream)
     assert rc == 0, pa.pa_last_error()
     torch.cuda.synchronize()
