@@ -504,7 +504,7 @@ def run_local(args, pa, runner, chunk: int = 512):
 CASCADE_METRIC = "cascade decode over a shared prefix: effective KV GB/s, bf16 paged KV, 1xMI355X"
 
 
-def run_cascade(args, pa):
+def run_cascade(args, pa, B=64, P=4096, suffix_range=(64, 1024)):
     """A decode step of 64 requests that share a 4096-token prefix (the
     shape the cascade is for: many requests, a long common prompt), each
     with its own 64-1024 tokens of history; 32 query / 8 KV heads of 128,
@@ -512,9 +512,9 @@ def run_cascade(args, pa):
     plain split decode + merge.  `value` is the plain path's K/V bytes (every
     key of every sequence) over the cascade's time; the roofline counts the
     bytes the cascade must read (the prefix once, each suffix once)."""
-    B, P, Hq, Hkv, D, bs, S = 64, 4096, 32, 8, 128, 16, 8
+    Hq, Hkv, D, bs, S = 32, 8, 128, 16, 8
     rng = np.random.Generator(np.random.PCG64(6))
-    suffix = rng.integers(64, 1024, size=B, endpoint=True)
+    suffix = rng.integers(suffix_range[0], suffix_range[1], size=B, endpoint=True)
     lens = P + suffix
     n = P // bs
     own = [-(-int(x) // bs) for x in suffix]
@@ -590,7 +590,8 @@ def run_cascade(args, pa):
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(t_c, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "cascade_decode_b64_prefix4096_suffix64-1024_h32-8-128_bs16",
+        "config": {"workload": f"cascade_decode_b{B}_prefix{P}_suffix{suffix_range[0]}-"
+                               f"{suffix_range[1]}_h32-8-128_bs16",
                    "num_seqs": B, "common_prefix_len": P, "context_tokens": int(lens.sum()),
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
                    "step": "paged_attn_cascade (prefix prefill + suffix prefill + merge)"},
@@ -606,12 +607,28 @@ def run_cascade(args, pa):
     }
 
 
+def run_cascade_sweep(args, pa):
+    """Cascade vs plain split decode over a grid of batch sizes, shared
+    prefix lengths and suffix ranges (the measurements behind the cascade
+    decision rule, pa_use_cascade).  One JSON object per point."""
+    rows = []
+    for B in (8, 16, 32, 64, 128):
+        for P in (256, 512, 1024, 2048, 4096, 8192):
+            for suf in ((1, 64), (64, 1024)):
+                r = run_cascade(args, pa, B=B, P=P, suffix_range=suf)
+                rows.append({"B": B, "P": P, "suffix": list(suf),
+                             "cascade_ms": r["ms_per_step"], "plain_ms": r["plain_decode"]["ms"]})
+                print(json.dumps(rows[-1]), flush=True)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "long", "cascade", "local"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "mixed", "long", "cascade", "cascade-sweep", "local"])
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
@@ -635,6 +652,9 @@ def main():
 
     if args.workload == "cascade":
         print(json.dumps(run_cascade(args, pa)), flush=True)
+        return
+    if args.workload == "cascade-sweep":
+        run_cascade_sweep(args, pa)
         return
     if args.workload == "local":
         print(json.dumps(run_local(args, pa, runner)), flush=True)

@@ -323,6 +323,35 @@ int scaled_fp8_quant(void* out, const void* input, const float* scale,
                      int64_t num_elems, pa_dtype_t dtype, void* stream);
 
 /*
+ * pa_use_cascade — HOST-side decision whether a batch should take
+ * paged_attn_cascade rather than the plain path [vLLM flash_attn.py
+ * (e2f56c3), use_cascade_attention].  The page's support checks, in its
+ * order: no cascade when common_prefix_len < 256, with ALiBi, a sliding
+ * window or chunked local attention, with fewer than 8 requests, or with
+ * decode context parallelism (dcp_world_size > 1).  Then, as on the page, a
+ * batch that would not take split-KV decode (a request with more than one
+ * query, or one query head per KV head) takes the cascade.  For a decode
+ * batch the page compares CTA waves of its kernels on `num_sms`
+ * multiprocessors; here the comparison is between time models of this
+ * library's two paths on MI355X (paged_attn_decode with splits +
+ * merge_attn_states against paged_attn_cascade), calibrated on measured
+ * times of decode batches of 8..128 requests with 256..8192 shared keys:
+ * fixed costs, unique and re-read K/V bytes, the prefix pass's MFMA work
+ * and the longest per-request suffix.
+ *
+ *   query_lens, seq_lens  HOST int32 [num_reqs]: new queries and keys
+ *                         (including the prefix) of each request.
+ *   kv_elem_bytes         2 for a 16-bit cache, 1 for fp8.
+ *   Returns 1 (use the cascade), 0 (do not), or a negative code.  No
+ *   device work.
+ */
+int pa_use_cascade(int common_prefix_len, const int32_t* query_lens,
+                   const int32_t* seq_lens, int num_reqs, int num_heads,
+                   int num_kv_heads, int head_size, int kv_elem_bytes,
+                   int use_alibi, int use_sliding_window,
+                   int use_local_attention, int dcp_world_size);
+
+/*
  * pa_local_virtual_batches — HOST-side rewriting of a batch for chunked
  * local attention [vLLM flash_attn.py (v0.9.0.1 docs),
  * make_local_attention_virtual_batches]: positions are cut into chunks of

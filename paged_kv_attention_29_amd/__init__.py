@@ -32,6 +32,7 @@ __all__ = [
     "merge_attn_states",
     "scaled_fp8_quant",
     "paged_attn_cascade",
+    "use_cascade",
     "local_virtual_batches",
     "check_indices",
     "pa_last_error",
@@ -75,10 +76,13 @@ def _load() -> ctypes.CDLL:
                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _vp,
                                        _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
     lib.scaled_fp8_quant.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp]
+    lib.pa_use_cascade.argtypes = [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _i32]
     lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
                                              _vp, _vp, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode",
                "paged_attn_decode_noalloc", "merge_attn_states", "scaled_fp8_quant",
+               "pa_use_cascade",
                "pa_check_indices", "paged_attn_cascade", "pa_local_virtual_batches"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
@@ -402,6 +406,27 @@ def scaled_fp8_quant(out: torch.Tensor, input: torch.Tensor, scale: torch.Tensor
     _check("scaled_fp8_quant", lib.scaled_fp8_quant(
         _ptr(out), _ptr(input), _ptr(scale), input.numel(), _code(input.dtype), _stream(stream)))
     return out
+
+
+def use_cascade(common_prefix_len: int, query_lens, seq_lens, num_heads: int,
+                num_kv_heads: int, head_size: int, kv_elem_bytes: int = 2,
+                use_alibi: bool = False, use_sliding_window: bool = False,
+                use_local_attention: bool = False, dcp_world_size: int = 1) -> bool:
+    """Whether a batch should take paged_attn_cascade (see pa_use_cascade):
+    host int arrays in, no device work."""
+    import numpy as np
+    ql = np.ascontiguousarray(query_lens, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if ql.shape != sl.shape:
+        raise ValueError("query_lens and seq_lens must have the same length")
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.pa_use_cascade(int(common_prefix_len), ptr(ql), ptr(sl), ql.size, int(num_heads),
+                            int(num_kv_heads), int(head_size), int(kv_elem_bytes), int(use_alibi),
+                            int(use_sliding_window), int(use_local_attention),
+                            int(dcp_world_size))
+    if rc < 0:
+        raise PagedAttnError("pa_use_cascade", rc, pa_last_error())
+    return rc == 1
 
 
 def local_virtual_batches(attn_chunk_size: int, query_start_loc, seq_lens, block_table,

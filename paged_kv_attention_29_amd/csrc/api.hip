@@ -482,6 +482,35 @@ int scaled_fp8_quant(void* out, const void* input, const float* scale, int64_t n
                     fn);
 }
 
+int pa_use_cascade(int common_prefix_len, const int32_t* query_lens, const int32_t* seq_lens,
+                   int num_reqs, int num_heads, int num_kv_heads, int head_size,
+                   int kv_elem_bytes, int use_alibi, int use_sliding_window,
+                   int use_local_attention, int dcp_world_size) {
+  const char* fn = "pa_use_cascade";
+  if (num_reqs < 0) return fail(PA_ERR_INVALID, "%s: num_reqs must be >= 0", fn);
+  if (num_reqs > 0 && (query_lens == nullptr || seq_lens == nullptr))
+    return fail(PA_ERR_INVALID, "%s: NULL query_lens or seq_lens", fn);
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_size <= 0 ||
+      (kv_elem_bytes != 1 && kv_elem_bytes != 2))
+    return fail(PA_ERR_INVALID, "%s: bad head counts, head_size or kv_elem_bytes", fn);
+  ok();
+  // the page's support checks, in its order
+  if (common_prefix_len < 256) return 0;
+  if (use_alibi || use_sliding_window || use_local_attention) return 0;
+  if (num_reqs < 8) return 0;
+  if (dcp_world_size > 1) return 0;
+  // not a split-decode batch (several queries per request, or one query
+  // head per KV head): the cascade saves the prefix re-reads
+  bool all_decode = true;
+  for (int b = 0; b < num_reqs; ++b) all_decode = all_decode && query_lens[b] == 1;
+  if (!(num_heads / num_kv_heads > 1 && all_decode)) return 1;
+  // a decode batch: the calibrated time models of the two paths
+  return pa::cascade_beats_split_decode(common_prefix_len, seq_lens, num_reqs, num_heads,
+                                        num_kv_heads, head_size, kv_elem_bytes)
+             ? 1
+             : 0;
+}
+
 int pa_local_virtual_batches(int attn_chunk_size, int block_size, const int32_t* query_start_loc,
                              const int32_t* seq_lens, int num_seqs, const int32_t* block_table,
                              int64_t block_table_stride, int block_table_cols, int max_virtual,

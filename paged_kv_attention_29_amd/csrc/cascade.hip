@@ -90,4 +90,36 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
                       p.head_size, p.dtype, p.dtype, stream);
 }
 
+// Cascade decision for a decode batch (one query per request), from time
+// models of the two paths calibrated on one MI355X (32 query / 8 KV heads of
+// 128, bf16, block 16; requests 8..128, shared prefixes 256..8192 keys, own
+// suffixes 1..1024 keys; non-negative least squares on relative error).
+// Bytes are K and V of every KV head; times in microseconds.
+//   plain split decode + merge: a fixed cost, the K/V bytes each key is
+//     read for once (HBM), and the re-reads of the shared prefix by the
+//     other requests (served mostly by the caches);
+//   cascade: a fixed cost (four launches), the prefix pass's MFMA work,
+//     the prefix bytes, the suffix bytes, and the longest suffix (the suffix
+//     pass runs one query per sequence, so its time follows its longest
+//     item).
+// Returns true when the modelled cascade time is the lower one.
+bool cascade_beats_split_decode(int prefix, const int32_t* seq_lens, int num_reqs, int num_heads,
+                                int num_kv_heads, int head_size, int kv_elem_bytes) {
+  const double row = (double)num_kv_heads * head_size * 2 * kv_elem_bytes;  // bytes per key
+  double suf_sum = 0, suf_max = 0;
+  for (int b = 0; b < num_reqs; ++b) {
+    const double s = seq_lens[b] > prefix ? seq_lens[b] - prefix : 0;
+    suf_sum += s;
+    suf_max = s > suf_max ? s : suf_max;
+  }
+  const double MB = 1e6;
+  const double unique = (prefix + suf_sum) * row / MB;
+  const double reread = (double)(num_reqs - 1) * prefix * row / MB;
+  const double gflop = 4.0 * head_size * num_heads * (double)num_reqs * prefix / 1e9;
+  const double t_plain = 14.702 + 0.17726 * unique + 0.10315 * reread;
+  const double t_cascade = 20.284 + 1.1570 * gflop + 0.15095 * suf_sum * row / MB +
+                           3.3735 * suf_max * row / MB + 0.14465 * prefix * row / MB;
+  return t_cascade < t_plain;
+}
+
 }  // namespace pa

@@ -88,6 +88,9 @@ int launch_prefill(const AttnParams& p, hipStream_t stream);
 // prefix-shared causal prefill (p.causal, no window / ALiBi): parts_out
 // [max_prefix_splits + 1, T, Hq, D] in p.dtype, parts_lse
 // [max_prefix_splits + 1, Hq, T], ints [num_seqs + 3]
+// host: the calibrated time comparison behind pa_use_cascade (decode batches)
+bool cascade_beats_split_decode(int prefix, const int32_t* seq_lens, int num_reqs, int num_heads,
+                                int num_kv_heads, int head_size, int kv_elem_bytes);
 int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void* parts_out,
                    float* parts_lse, int32_t* ints, hipStream_t stream);
 
