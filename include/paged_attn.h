@@ -192,7 +192,9 @@ int paged_attn_prefill(void* out, float* lse, const void* q,
  *   kv_cache_dtype, k_scale, v_scale: a 16-bit cache (= dtype) or an fp8
  *   cache with its scales (see the conventions above); the K scale
  *   multiplies every score and the V scale the result.
- *   num_heads / num_kv_heads must be at most 16.
+ *   num_heads / num_kv_heads must be at most 128 [vLLM flash_attn.py
+ *   (e2f56c3), FlashAttentionImpl.__init__: any num_queries_per_kv =
+ *   num_heads / num_kv_heads].
  */
 int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
                       const void* q, const void* key_cache,

@@ -126,8 +126,13 @@ int check_decode(const char* fn, int num_seqs, int max_seq_len, int num_heads, i
   if (rc != PA_OK) return rc;
   if (num_splits < 1 || num_splits > 256)
     return fail(PA_ERR_INVALID, "%s: num_splits must be in [1, 256] (got %d)", fn, num_splits);
-  if (num_heads / num_kv_heads > 16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
+  if (num_heads / num_kv_heads > 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 128 query heads per KV head", fn);
+  // work items (KV heads x groups of 16 query heads x sequences x splits)
+  // form a one-dimensional grid
+  if ((int64_t)num_kv_heads * ((num_heads / num_kv_heads + 15) / 16) * num_seqs * num_splits >
+      INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: too many work items for one grid", fn);
   if (max_seq_len < 0) return fail(PA_ERR_INVALID, "%s: max_seq_len must be >= 0", fn);
   if (max_seq_len >= (1 << 24))
     return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);

@@ -47,6 +47,9 @@ struct DecodeArgs {
   const int32_t* block_table;
   int64_t bt_stride;
   int B, Hq, Hkv, G, bs, S;
+  // query heads of a KV head beyond 16 are split into column groups of 16:
+  // CG groups per KV head (1 when G <= 16), each its own work item
+  int CG;
   int chunk;            // keys per split (block-aligned, from the batch bound)
   uint32_t bs_magic;    // ceil(2^32 / bs)
   float scale_log2;     // scale * log2(e)
@@ -72,7 +75,11 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 // A work item covers HPW adjacent KV heads (2 when the head counts allow it
 // and D <= 128): each key row of the item is then 2 * 256 contiguous bytes,
 // which the memory system streams faster than 256-byte rows 2 KB apart.
-// Their query heads are the first G * HPW columns of the MFMA tile.
+// Their query heads are the first G * HPW columns of the MFMA tile.  With
+// more than 16 query heads per KV head (HPW = 1) an item covers one group
+// of 16 of them (the last group may be smaller), and the groups of a KV
+// head are consecutive items, so the K/V bytes they share are read from
+// HBM once and then from the caches.
 // Keys per iteration: NT MFMA row tiles of 16, so that a wave keeps 16 KB of
 // K/V in flight while it computes the previous step (one tile for two heads
 // or D = 256; an fp8 cache at D = 256, whose rows are half as long and
@@ -92,7 +99,8 @@ constexpr size_t vslab_bytes() {
 }
 template <int D, int HPW>
 constexpr size_t comb_bytes(int G) {
-  return (size_t)kWaves * G * HPW * (D + 4) * 4;
+  const int cols = G * HPW < 16 ? G * HPW : 16;  // columns of one item
+  return (size_t)kWaves * cols * (D + 4) * 4;
 }
 // The combine runs after the key loop and reuses the V slabs.  The
 // work-item ranking runs before both (scratch ints at the start, below) and
@@ -157,7 +165,7 @@ static_assert((kRankMaxS + 1 + kRankMaxB) * 4 <= kRankScratchBytes, "ranking scr
 // wave 0 only; sh = LDS scratch, res = the hand-off slot (4 ints)
 template <int HPW>
 __device__ void ranked_item_wave0(const DecodeArgs& a, int* sh, int* res) {
-  const int S = a.S, B = a.B, HG = a.Hkv / HPW;
+  const int S = a.S, B = a.B, HG = a.Hkv / HPW * a.CG;
   const int lane = threadIdx.x & 63;
   int* cnt = sh;                  // [S + 1] difference counts
   int* lens = sh + kRankMaxS + 1; // [B]
@@ -228,7 +236,7 @@ __device__ void ranked_item_wave0(const DecodeArgs& a, int* sh, int* res) {
   // of them; sel < 0 would mean inconsistent lengths and makes the kernel
   // exit)
   if (lane == 0) {
-    res[0] = g * HPW;
+    res[0] = g;
     res[1] = sel;
     res[2] = split;
     res[3] = sel >= 0 ? lens[sel] : 0;
@@ -280,19 +288,26 @@ struct Dec {
     }
   }
 
-  // KV heads g0 .. g0 + HPW - 1 of sequence b, keys [lo_vis, hi) of `split`
+  // KV heads g0 .. g0 + HPW - 1 of sequence b, keys [lo_vis, hi) of `split`;
+  // its columns are query heads hb .. hb + nc - 1
   struct Item {
     int g0, b, split;
+    int hb, nc;
     int pos;             // the query's position, L - 1
     int lo_vis, hi;
     int s_begin, s_end;  // steps of KPS keys that cover [lo_vis, hi)
     int last_j0;         // first key of the split's last tile of 16
   };
 
-  static __device__ __forceinline__ Item make_item(const DecodeArgs& a, int g0, int b,
+  // grp: the item's column group, (KV head group) * CG + (group of 16)
+  static __device__ __forceinline__ Item make_item(const DecodeArgs& a, int grp, int b,
                                                    int split, int L) {
     Item it;
-    it.g0 = g0;
+    const int kvg = grp / a.CG;
+    const int cg = grp - kvg * a.CG;
+    it.g0 = kvg * HPW;
+    it.hb = it.g0 * a.G + 16 * cg;
+    it.nc = HPW == 2 ? 2 * a.G : min(16, a.G - 16 * cg);
     it.b = b;
     it.split = split;
     it.pos = L - 1;
@@ -371,7 +386,7 @@ struct Dec {
   using QRaw = std::conditional_t<Q8, u32x2, v8s>;
   static __device__ __forceinline__ void load_q(const DecodeArgs& a, const Item& it, int r16,
                                                 int c4, QRaw (&qraw)[KK]) {
-    const int hq = it.g0 * a.G + (r16 < a.G * HPW ? r16 : 0);
+    const int hq = it.hb + (r16 < it.nc ? r16 : 0);
     if constexpr (Q8) {
       const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)it.b * a.Hq + hq) * D;
 #pragma unroll
@@ -406,7 +421,7 @@ struct Dec {
   // ALiBi slope of this lane's column, in log2 units
   static __device__ __forceinline__ float slope_of(const DecodeArgs& a, const Item& it, int r16) {
     if constexpr (ALIBI)
-      return r16 < a.G * HPW ? a.alibi[it.g0 * a.G + r16] * kLog2e : 0.0f;
+      return r16 < it.nc ? a.alibi[it.hb + r16] * kLog2e : 0.0f;
     else
       return 0.0f;
   }
@@ -535,10 +550,10 @@ struct Dec {
     wave_lds_sync();
   }
 
-  // Result of column j (query head g0 * G + j), elements d .. d + 3.
-  static __device__ __forceinline__ void emit4(const DecodeArgs& a, int g0, int b, int split,
+  // Result of column j (query head hb + j), elements d .. d + 3.
+  static __device__ __forceinline__ void emit4(const DecodeArgs& a, int hb, int b, int split,
                                                int j, int d, v4f val, float lse) {
-    const int h = g0 * a.G + j;
+    const int h = hb + j;
     if (a.S > 1) {
       *reinterpret_cast<v4f*>(a.part_out + (((int64_t)split * a.B + b) * a.Hq + h) * D + d) = val;
       if (d == 0) a.part_lse[((int64_t)split * a.Hq + h) * a.B + b] = lse;
@@ -550,17 +565,16 @@ struct Dec {
   }
   // Sink logit of column j in log2 units, or -inf (no sinks, or a split
   // other than 0).
-  static __device__ __forceinline__ float sink_of(const DecodeArgs& a, int g0, int split, int j) {
-    return a.sinks != nullptr && split == 0 ? a.sinks[g0 * a.G + j] * kLog2e : kNegInf;
+  static __device__ __forceinline__ float sink_of(const DecodeArgs& a, int hb, int split, int j) {
+    return a.sinks != nullptr && split == 0 ? a.sinks[hb + j] * kLog2e : kNegInf;
   }
   // An item without visible keys: zero output, log-sum-exp -inf (or the
   // sink in split 0).
-  static __device__ __forceinline__ void emit_empty(const DecodeArgs& a, int g0, int b,
-                                                    int split) {
-    for (int idx = threadIdx.x; idx < a.G * HPW * (D / 4); idx += kWaves * 64) {
+  static __device__ __forceinline__ void emit_empty(const DecodeArgs& a, const Item& it) {
+    for (int idx = threadIdx.x; idx < it.nc * (D / 4); idx += kWaves * 64) {
       const int j = idx / (D / 4);
-      emit4(a, g0, b, split, j, (idx - j * (D / 4)) * 4, v4f{0.f, 0.f, 0.f, 0.f},
-            sink_of(a, g0, split, j) * kLn2);
+      emit4(a, it.hb, it.b, it.split, j, (idx - j * (D / 4)) * 4, v4f{0.f, 0.f, 0.f, 0.f},
+            sink_of(a, it.hb, it.split, j) * kLn2);
     }
   }
 
@@ -572,7 +586,7 @@ struct Dec {
                                                       int wave, int r16, int c4, float m_run,
                                                       float l_run, const v4f (&o)[DC],
                                                       float* comb) {
-    const int GC = a.G * HPW;
+    const int GC = it.nc;
     float l_tot = l_run + shfl_xor(l_run, 16);
     l_tot += shfl_xor(l_tot, 32);
     __syncthreads();
@@ -588,7 +602,7 @@ struct Dec {
       const int j = idx / (D / 4);
       const int d = (idx - j * (D / 4)) * 4;
       f2 ml[kWaves];
-      const float sk = sink_of(a, it.g0, it.split, j);  // (max sk, sum 1, output 0)
+      const float sk = sink_of(a, it.hb, it.split, j);  // (max sk, sum 1, output 0)
       float M = sk;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -609,7 +623,7 @@ struct Dec {
       // (an fp8 cache's V scale multiplies the result)
       const float inv = den > 0.f ? (F8 ? *a.v_scale : 1.0f) / den : 0.f;
       const float lse = den > 0.f ? (M + __log2f(den)) * kLn2 : kNegInf;
-      emit4(a, it.g0, it.b, it.split, j, d, num * inv, lse);
+      emit4(a, it.hb, it.b, it.split, j, d, num * inv, lse);
     }
   }
 };
@@ -643,33 +657,33 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   const int r16 = lane & 15;   // key row of the K piece / head column of the tile
   const int c4 = lane >> 4;    // which quarter: keys 4*c4..4*c4+3 of S^T, D piece of K
 
-  int g0, b, split, L;
+  int grp, b, split, L;  // column group, sequence, split, length
   if (a.B <= kRankMaxB && a.S <= kRankMaxS) {
     int* res = reinterpret_cast<int*>(smem + rank_slot_offset<D, HPW, K::F8>(a.G));
     if (wave == 0) ranked_item_wave0<HPW>(a, reinterpret_cast<int*>(smem), res);
     __syncthreads();
-    g0 = __builtin_amdgcn_readfirstlane(res[0]);
+    grp = __builtin_amdgcn_readfirstlane(res[0]);
     b = __builtin_amdgcn_readfirstlane(res[1]);
     split = __builtin_amdgcn_readfirstlane(res[2]);
     L = __builtin_amdgcn_readfirstlane(res[3]);
     if (b < 0) return;
   } else {
-    const int HG = a.Hkv / HPW;
+    const int HG = a.Hkv / HPW * a.CG;
     const int per_split = HG * a.B;
     split = blockIdx.x / per_split;
     int j = blockIdx.x - split * per_split - static_cast<int>((int64_t)split * HG % per_split);
     if (j < 0) j += per_split;
-    g0 = (j % HG) * HPW;  // first KV head of the item
+    grp = j % HG;
     b = j / HG;
     L = a.seq_lens[b];
   }
 
-  const typename K::Item it = K::make_item(a, g0, b, split, L);
+  const typename K::Item it = K::make_item(a, grp, b, split, L);
   if (it.lo_vis >= it.hi) {
-    K::emit_empty(a, g0, b, split);
+    K::emit_empty(a, it);
     return;
   }
-  const bool col_ok = r16 < a.G * HPW;
+  const bool col_ok = r16 < it.nc;
   const int hsel = r16 / a.G;  // which of the item's KV heads the column reads
   const float slope_log2 = K::slope_of(a, it, r16);
 
@@ -715,7 +729,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
 template <typename T, int D, int FEAT, int HPW>
 int launch_h(const DecodeArgs& args, hipStream_t stream) {
   constexpr bool F8 = (FEAT & kFp8) != 0;
-  const int64_t items = (int64_t)(args.Hkv / HPW) * args.B * args.S;
+  const int64_t items = (int64_t)(args.Hkv / HPW) * args.CG * args.B * args.S;
   const size_t lds = decode_lds_bytes<D, HPW, F8>(args.G);
   if (lds > 65536) {
     // (the fp8 D = 256 variants with two tiles per step use more than 64 KB)
@@ -775,6 +789,7 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.Hq = p.num_heads;
   a.Hkv = p.num_kv_heads;
   a.G = p.num_heads / p.num_kv_heads;
+  a.CG = (a.G + 15) / 16;
   a.bs = p.block_size;
   a.S = p.num_splits;
   {

@@ -77,7 +77,7 @@ def _prefill(pa, **kw):
     (dict(bs=24), -1), (dict(bs=0), -1), (dict(bs=512), -2),
     (dict(hq=6, hkv=4), -1), (dict(d=96), -2), (dict(dtype=2), -2), (dict(dtype=7), -2),
     (dict(out=None), -1), (dict(splits=2), -1), (dict(splits=0), -1), (dict(splits=300), -1),
-    (dict(hq=34, hkv=2), -2), (dict(wl=-2), -1), (dict(cap=-1.0), -1),
+    (dict(hq=258, hkv=2), -2), (dict(wl=-2), -1), (dict(cap=-1.0), -1),
     (dict(scale=float("inf")), -1), (dict(q=None), -1), (dict(bt_stride=0), -1),
 ])
 def test_decode_validation(lib, kw, code):

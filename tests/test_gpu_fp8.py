@@ -87,6 +87,9 @@ DECODE = [
      False, True, 4),
     ("g8_d256_fp16_unsplit", [1, 999, 260], 16, 2, 256, 32, torch.float16, -1, 0.0, False, False,
      1),
+    # 32 query heads on one KV head (two column groups), with sinks
+    ("g32_d128_mqa_sinks", [17, 900, 2500], 32, 1, 128, 16, torch.bfloat16, -1, 0.0, False, True,
+     2),
 ]
 
 

@@ -216,6 +216,12 @@ DECODE_EDGES = [
     ("window0", [50, 3], 4, 2, 64, 16, torch.bfloat16, 0, 0.0, False, 2),
     ("empty_splits", [5, 20], 8, 2, 128, 16, torch.bfloat16, -1, 1.0, True, 9),
     ("bs256", [700, 300], 6, 2, 64, 256, torch.float16, -1, 0.0, False, 2),
+    # more than 16 query heads per KV head: column groups of 16 per item
+    ("g32_mqa_d128", [31, 200, 2000, 1], 32, 1, 128, 16, torch.bfloat16, -1, 0.0, False, 4),
+    ("g64_d128_alibi", [500, 77, 1300], 64, 1, 128, 16, torch.bfloat16, -1, 0.0, True, 2),
+    ("g20_d64_window_cap", [300, 1000, 5], 40, 2, 64, 32, torch.float16, 99, 5.0, False, 3),
+    ("g128_d64", [129, 700], 128, 1, 64, 16, torch.bfloat16, -1, 0.0, False, 1),
+    ("g48_d256_alibi", [400, 33], 96, 2, 256, 16, torch.bfloat16, -1, 0.0, True, 2),
 ]
 
 

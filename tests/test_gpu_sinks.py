@@ -95,6 +95,7 @@ DECODE = [
     ("g4_d128_s4", [0, 1, 17, 300, 1024], 32, 8, 128, 16, torch.bfloat16, -1, 0.0, 4),
     ("g8_d64_window_s3", [5, 700, 64], 16, 2, 64, 32, torch.float16, 40, 3.0, 3),
     ("g1_d256_s2", [0, 33, 260], 4, 4, 256, 16, torch.bfloat16, -1, 0.0, 2),
+    ("g24_d128_s3", [0, 40, 900], 48, 2, 128, 16, torch.bfloat16, -1, 0.0, 3),
 ]
 
 
