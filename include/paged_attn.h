@@ -143,8 +143,10 @@ int reshape_and_cache(const void* key, const void* value,
  *                   result, and the products run on the 16-bit values of
  *                   the codes (exact), as for a 16-bit cache.
  *   PA_ERR_UNSUPPORTED also for num_seqs > 65535, more than 128 query heads
- *   per KV head, max_seqlen_k >= 2^24 or num_kv_heads * max_seqlen_q >=
- *   2^31 (grid limits).
+ *   per KV head, max_seqlen_k >= 2^24, num_kv_heads * max_seqlen_q >= 2^31
+ *   or num_kv_heads * (total_q + num_seqs) >= 2^31 (grid limits).  The
+ *   grid is sized from total_q, so cu_seqlens_q[num_seqs] must not exceed
+ *   total_q (q's row count).
  */
 int paged_attn_prefill(void* out, float* lse, const void* q,
                        const void* key_cache, const void* value_cache,
@@ -292,8 +294,8 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
  *   parts_lse          fp32 workspace [max_prefix_splits + 1, num_heads,
  *                      total_q];
  *   work_ints          int32 workspace [num_seqs + 3].
- *   Workspaces are caller-owned and overwritten; num_kv_heads * total_q must
- *   be below 2^31.
+ *   Workspaces are caller-owned and overwritten; num_kv_heads * (total_q +
+ *   num_seqs) must be below 2^31.
  */
 int paged_attn_cascade(void* out, float* lse, const void* q,
                        const void* key_cache, const void* value_cache,

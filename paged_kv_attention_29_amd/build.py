@@ -20,6 +20,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source additions.  The prefill kernel assumes no NaN among its inputs:
+# its row maxima then compile to plain v_max3 chains, without the operand
+# quieting IEEE maxNum otherwise needs (a NaN input gives a NaN-or-garbage
+# result either way).
+EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:
@@ -43,7 +48,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
         for r in ex.map(_run, cmds):

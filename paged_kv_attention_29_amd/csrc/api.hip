@@ -255,6 +255,9 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const void* key_cac
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 sequences in one call", fn);
   if ((int64_t)num_kv_heads * max_seqlen_q > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads * max_seqlen_q must be below 2^31", fn);
+  if ((int64_t)num_kv_heads * (total_q + num_seqs) > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads * (total_q + num_seqs) must be below 2^31",
+                fn);
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
   pa::AttnParams p{};
   p.out = out;
@@ -433,9 +436,11 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
     return fail(PA_ERR_UNSUPPORTED, "%s: sequences of 2^24 keys or more are not supported", fn);
   if (num_seqs > 65535)
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 sequences in one call", fn);
-  // the prefix pass takes every query as one sequence
-  if ((int64_t)num_kv_heads * total_q > INT32_MAX)
-    return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads * total_q must be below 2^31", fn);
+  // the prefix pass takes every query as one sequence; the suffix pass's
+  // grid has up to total_q + num_seqs query tiles per KV head
+  if ((int64_t)num_kv_heads * (total_q + num_seqs) > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads * (total_q + num_seqs) must be below 2^31",
+                fn);
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
   pa::AttnParams p{};
   p.out = out;

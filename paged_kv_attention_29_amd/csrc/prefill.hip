@@ -37,7 +37,8 @@
 #include "common.h"
 #include "launch.h"
 
-#include <type_traits>  // std::true_type
+#include <climits>      // INT_MAX, INT_MIN
+#include <type_traits>  // std::true_type, std::integral_constant
 
 namespace pa {
 
@@ -62,7 +63,7 @@ struct PrefillArgs {
   const int32_t* block_table;
   int64_t bt_stride;
   int64_t total_q;
-  int B, Hq, Hkv, G, bs, tok_per_tile, n_qtiles;
+  int B, Hq, Hkv, G, bs, tok_per_tile;
   uint32_t bs_magic;
   float scale_log2;     // scale * log2(e)
   float cap_k2;         // 2 log2(e) scale / softcap
@@ -189,6 +190,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
+// Operand reads at an LDS byte address held as an integer: a lane's base
+// address (in a register) plus a constant, which becomes the instruction's
+// immediate offset.
+using lds_v8s = __attribute__((address_space(3))) const v8s;
+using lds_v4s = __attribute__((address_space(3))) v4s;
+__device__ __forceinline__ v8s lds_load16(uint32_t addr) { return *(lds_v8s*)(addr); }
+// ds_read_b64_tr_b16 (the lane layout of lds_read_tr16)
+__device__ __forceinline__ v4s lds_load_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(addr));
+}
+
 // wait until at most N vector-memory loads of this wave are outstanding
 // (asm, so it stays ordered with the untracked loads and their claims)
 template <int N>
@@ -237,21 +249,54 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     a.cap_k2 *= qs;
   }
 
-  // Grid (Hkv * query tiles, sequences), x = tile' * Hkv + g.  Workgroups are
-  // dispatched to the 8 XCDs round-robin in linear order, so with 8 KV heads
-  // XCD g runs every workgroup of head g.  The sequence is the outer index,
-  // so an XCD works through one sequence's query tiles together and the
-  // sequence's K/V for that head (512 B per key at D = 128) stays in the
-  // XCD's L2 while they run.  Inside a sequence the long (late) tiles go
-  // first (tile' counts down from the last tile).
+  // Grid x = t * Hkv + g over a compact list of query tiles t: sequence b
+  // owns tiles [S_b, S_b + n_b) with S_b = floor(cu_q[b] / tok) + b and
+  // n_b = ceil(nq_b / tok), ranges that are disjoint, increase with b and
+  // lie below floor(total_q / tok) + B, so the grid holds at most one empty
+  // slot per sequence however uneven the lengths.  Workgroups are dispatched
+  // to the 8 XCDs round-robin in linear order, so with 8 KV heads XCD g runs
+  // every workgroup of head g; the sequence is the outer index, so an XCD
+  // works through one sequence's query tiles together and the sequence's
+  // K/V for that head stays in the XCD's L2 while they run.  Inside a
+  // sequence the long (late) tiles go first.
   const int g = blockIdx.x % a.Hkv;
-  const int qt = a.n_qtiles - 1 - static_cast<int>(blockIdx.x / a.Hkv);
-  const int b = blockIdx.y;
-  const int q0 = a.cu_q[b];
-  const int nq = a.cu_q[b + 1] - q0;
-  const int tok0 = qt * a.tok_per_tile;
-  if (tok0 >= nq) return;
-  const int L = a.seq_lens[b];
+  const int t = static_cast<int>(blockIdx.x / a.Hkv);
+  const int tok = a.tok_per_tile;
+  // The last b with S_b <= t, by a wave-parallel search: each round splits
+  // the candidate range [lo, lo + span) into 64 parts and keeps the last
+  // part whose first S is <= t (one round up to 64 sequences, three up to
+  // 2^18).  The final round also reads the sequence's bounds and length,
+  // and the block id of this wave's first key group (keys RW * wave ..),
+  // which the first tile needs whenever the key range starts at key 0.
+  const int wave_blk = wave * RW / a.bs;  // block-table column of that group
+  int lo = 0, span = a.B, q0 = 0, q1 = 0, L = 0, blk0 = 0;
+  for (;;) {
+    const int step = (span + 63) / 64;
+    const int c = lo + lane * step;
+    const bool in = lane * step < span;
+    const bool fin = in && step == 1;
+    const int cq = in ? a.cu_q[c] : 0;
+    const int cq1 = fin ? a.cu_q[c + 1] : 0;
+    const int cl = fin ? a.seq_lens[c] : 0;
+    const int cb = fin && wave_blk < a.bt_stride ? a.block_table[(int64_t)c * a.bt_stride + wave_blk] : 0;
+    const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in && cq / tok + c <= t));
+    if (k == 0) return;  // below S_0 (cu_q[0] > 0)
+    lo += (k - 1) * step;
+    if (step == 1) {
+      q0 = __builtin_amdgcn_readlane(cq, k - 1);
+      q1 = __builtin_amdgcn_readlane(cq1, k - 1);
+      L = __builtin_amdgcn_readlane(cl, k - 1);
+      blk0 = __builtin_amdgcn_readlane(cb, k - 1);
+      break;
+    }
+    span = min(step, span - (k - 1) * step);
+  }
+  const int b = lo;
+  const int nq = q1 - q0;
+  const int local = t - (q0 / tok + b);
+  if (local >= (nq + tok - 1) / tok) return;  // an empty slot
+  const int qt = (nq + tok - 1) / tok - 1 - local;
+  const int tok0 = qt * tok;
   const int ctx = L - nq;
   const int ntok = min(nq - tok0, a.tok_per_tile);
   const int p_first = ctx + tok0;
@@ -288,39 +333,14 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   const int32_t* btab = a.block_table + (int64_t)b * a.bt_stride;
   // first key this wave fetches in a tile (clamped to the last key; the
   // other rows follow it inside the same 16-key group, hence the same block)
-  auto group_key = [&](int tile) { return min(tile * kKT + wave * RW, L - 1); };
+  auto group_key = [&](int tile) { return max(min(tile * kKT + wave * RW, L - 1), 0); };
   // Block ids of this wave's key group for tiles t0 + [0, 64): lane t holds
   // tile t0 + t (clamped to the last tile).  Loaded ahead in one vector load
   // and read with v_readlane, so the loop issues no scalar loads.
   auto load_ids = [&](int t0) -> uint32_t {
-    const int tile = min(t0 + lane, t_end - 1);
+    const int tile = max(min(t0 + lane, t_end - 1), 0);
     return load4_async(btab + div_magic(group_key(tile), a.bs_magic));
   };
-  uint32_t ids = 0;
-  if (t_end > t_begin) ids = load_ids(t_begin);
-
-  // Q fragments (B operand of S^T = K Q^T).  Loaded by asm, like the K/V
-  // DMA: a load the compiler tracks would get a wait at its first use that
-  // also counts the DMAs in flight.  They complete before the prologue's
-  // DMA wait (loads complete in order) and are claimed after it.
-  v8s qf[KQ];
-  u32x2 q8[Q8 ? KQ : 1];  // an fp8 query's codes, widened after the wait
-  {
-    const int64_t qtok = row_ok ? q0 + tok0 + tk : q0;  // rows past the tile read a valid row
-    if constexpr (Q8) {
-      const uint8_t* qrow =
-          reinterpret_cast<const uint8_t*>(a.q) + (qtok * a.Hq + head) * D + 8 * g2;
-#pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) q8[kk] = load8_async(qrow + 16 * kk);
-    } else {
-      const uint16_t* qrow = a.q + (qtok * a.Hq + head) * D + 8 * g2;
-#pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) qf[kk] = load16_async(qrow + 16 * kk);
-    }
-  }
-  wait_vmcnt<KQ>();  // the block ids (issued before Q) landed
-  claim(ids);
-
   const char* kc = reinterpret_cast<const char*>(a.kc) + (int64_t)g * RBC;
   const char* vc = reinterpret_cast<const char*>(a.vc) + (int64_t)g * RBC;
 
@@ -345,6 +365,8 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     dma_k[i] = rr * row_bytes + dma_kp(i);
     dma_v[i] = rr * row_bytes + dma_vp(i);
   }
+  // block ids of this wave's key groups for 64 tiles (lane t: tile t0 + t)
+  uint32_t ids = 0;
   // block id of relative tile jt (< 64 past the loaded chunk's start)
   auto id_of = [&](int jt) { return __builtin_amdgcn_readlane(static_cast<int>(ids), jt & 63); };
   auto issue_tile = [&](int tile, int blk, int stage) {
@@ -373,6 +395,47 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     }
   };
 
+  // ---- prologue loads.  When the key range starts at key 0 and this wave's
+  //      first group lies inside the sequence, tile 0's block id came with
+  //      the sequence lookup and its K/V go out first; the block ids of the
+  //      later tiles and Q follow.  Otherwise the ids come first and tile 0
+  //      waits for them.  (t_begin < t_end whenever the tile has a query
+  //      row, its own key being visible; only an empty key split has none.)
+  static_assert(NST == 2, "the prologue fills one stage ahead");
+  const int n = t_end - t_begin;
+  const bool early = n > 0 && t_begin == 0 && wave * RW <= L - 1 && wave_blk < a.bt_stride;
+  if (early) issue_tile(t_begin, blk0, 0);
+  // (loaded unconditionally, an in-range entry even without tiles, so that
+  // ids has one definition up to its claim after the prologue's wait: a
+  // merge of two definitions could copy the register while it is loading)
+  ids = load_ids(t_begin);
+  // Q fragments (B operand of S^T = K Q^T).  Loaded by asm, like the K/V
+  // DMA: a load the compiler tracks would get a wait at its first use that
+  // also counts the DMAs in flight.  They complete before the prologue's
+  // final wait (loads complete in order) and are claimed after it.
+  v8s qf[KQ];
+  u32x2 q8[Q8 ? KQ : 1];  // an fp8 query's codes, widened after the wait
+  {
+    const int64_t qtok = row_ok ? q0 + tok0 + tk : q0;  // rows past the tile read a valid row
+    if constexpr (Q8) {
+      const uint8_t* qrow =
+          reinterpret_cast<const uint8_t*>(a.q) + (qtok * a.Hq + head) * D + 8 * g2;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) q8[kk] = load8_async(qrow + 16 * kk);
+    } else {
+      const uint16_t* qrow = a.q + (qtok * a.Hq + head) * D + 8 * g2;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) qf[kk] = load16_async(qrow + 16 * kk);
+    }
+  }
+  if (!early && n > 0) {
+    // tile 0's block id once the ids (issued before Q) landed: the wait and
+    // the read are one asm block, so nothing reads the loading register
+    int blk;
+    asm volatile("s_waitcnt vmcnt(%1)\n\tv_readfirstlane_b32 %0, %2" : "=s"(blk) : "i"(KQ), "v"(ids));
+    issue_tile(t_begin, blk, 0);
+  }
+
   float m_run = kNegInf;   // reference maximum of the row (log2 units)
   float l_run = 0.0f;      // this lane's half of the row sum
   v16f oacc[DC];
@@ -385,19 +448,20 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   // the finished log2-unit logit with cz = 1
   const float cz = (SOFTCAP || ALIBI) ? 1.0f : a.scale_log2;
   // does any row of this wave see a key of the tile starting at kbase?
-  auto tile_active = [&](int kbase) {
-    bool act = w_rows;
-    if (a.causal) act = act && kbase <= w_pmax;
-    if (a.window_left >= 0) act = act && kbase + kKT - 1 >= w_pmin - a.window_left;
-    return act;
-  };
+  // (wave-uniform: the bounds are kept in scalar registers)
+  const int act_hi = __builtin_amdgcn_readfirstlane(!w_rows ? -1 : a.causal ? w_pmax : INT_MAX);
+  const int act_lo = __builtin_amdgcn_readfirstlane(
+      a.window_left >= 0 ? static_cast<int>(max(static_cast<int64_t>(w_pmin) - a.window_left - (kKT - 1),
+                                                static_cast<int64_t>(INT_MIN)))
+                         : INT_MIN);
+  auto tile_active = [&](int kbase) { return kbase <= act_hi && kbase >= act_lo; };
 
   // ---- K operand of S^T = K Q^T: rows h2*32 + r32 of the tile, 16-byte piece
   //      2*kk + g2 (swizzled); rows r32 and 32 + r32 share the swizzle
   uint32_t k_lane[KQ];
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk)
-    k_lane[kk] = r32 * RB + 16 * ((2 * kk + g2) ^ swz_k<D>(r32));
+    k_lane[kk] = smem0 + r32 * RB + 16 * ((2 * kk + g2) ^ swz_k<D>(r32));
 
   // ---- V operand of O^T += V^T P^T: step s holds V[16s + 4*g2 + [0,4)][d] and
   //      V[16s + 8 + 4*g2 + [0,4)][d] for d = dc*32 + r32, two transpose reads.
@@ -413,16 +477,17 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // head dim within a chunk
     const int x = swz_v<D>(vr) >> 2;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) v_lane[m] = vr * RB + 64 * (m ^ x) + 16 * (vd >> 3) + 2 * (vd & 7);
+    for (int m = 0; m < NM; ++m)
+      v_lane[m] = smem0 + vr * RB + 64 * (m ^ x) + 16 * (vd >> 3) + 2 * (vd & 7);
   }
 
   // ---- softmax of one tile's scores (lane holds keys
-  //      kbase + 32*h2 + 8*(e/4) + 4*g2 + e%4 of its row): logits, masks on
-  //      tiles that cut a row's visible range, lazy rescale, probabilities
-  //      packed as the B operand of the PV product
-  auto softmax = [&](v16f* sacc, int kbase, v8s* pb) {
-    const bool need_mask = kbase + kKT > L || (a.causal && kbase + kKT - 1 > w_pmin) ||
-                           (a.window_left >= 0 && kbase < w_pmax - a.window_left);
+  //      kbase + 32*h2 + 8*(e/4) + 4*g2 + e%4 of its row): logits, masks
+  //      (MASKED: the tile cuts a row's visible range), lazy rescale,
+  //      probabilities packed as the B operand of the PV product
+  float neg_m = 0.0f;  // -m_run, or 0 while m_run = -inf
+  auto softmax = [&](v16f* sacc, int kbase, v8s* pb, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -434,7 +499,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
         if constexpr (ALIBI) z -= slope_log2 * static_cast<float>(abs(pos - key));
         sacc[h2][e] = z;
       }
-    if (need_mask) {
+    if constexpr (MASKED) {
       if (a.window_left < 0) {
         // one bound (no window): the key at offset o of the lane's pattern is
         // visible iff o <= hi_row - kbase - 4*g2 (o is an inline constant)
@@ -456,22 +521,17 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
           }
       }
     }
-    // row max: a max3 tree over the lane's 32 scores, then the other half of
-    // the row (lane ^ 32) through a lane swap
-    float m1[11];
+    // row max: three-input maxima over the lane's 32 scores (16 of them),
+    // then the other half of the row (lane ^ 32) through a lane swap
+    auto sc = [&](int i) { return sacc[i >> 4][i & 15]; };
+    float m1[10];
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      const int e = 3 * i;
-      m1[i] = fmaxf(fmaxf(sacc[e >> 4][e & 15], sacc[(e + 1) >> 4][(e + 1) & 15]),
-                    sacc[(e + 2) >> 4][(e + 2) & 15]);
-    }
-    m1[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    for (int i = 0; i < 10; ++i) m1[i] = fmaxf(fmaxf(sc(3 * i), sc(3 * i + 1)), sc(3 * i + 2));
     const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
     const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
     const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
-    const float m2d = fmaxf(m1[9], m1[10]);
-    float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
-    mx = fmaxf(mx, swap_halves_max(mx));
+    const float m2d = fmaxf(fmaxf(m1[9], sc(30)), sc(31));
+    const float mx = swap_halves_max(fmaxf(fmaxf(fmaxf(m2a, m2b), m2c), m2d));
     const float m_tile = mx * cz;
 
     // lazy rescale: move the reference only when the max grew a lot; rows
@@ -489,10 +549,12 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
         for (int dc = 0; dc < DC; ++dc) oacc[dc] *= alpha;
       }
       m_run = m_new;
+      neg_m = m_run == kNegInf ? 0.0f : -m_run;
     }
-    const float neg_m = m_run == kNegInf ? 0.0f : -m_run;
 
-    float ps[4];  // sums of the rounded probabilities the PV product uses
+    // probabilities; the row sum adds the rounded values the PV product
+    // uses, in two chains (the first continues the running sum)
+    float ps[2] = {l_run, 0.0f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float pv[8];
@@ -500,72 +562,75 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], cz, neg_m));
       u32x4 w = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
                  T::pack2(pv[6], pv[7])};
-      ps[s] = T::sum2(w[3], T::sum2(w[2], T::sum2(w[1], T::sum2(w[0], 0.0f))));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[s & 1] = T::sum2(w[i], ps[s & 1]);
       pb[s] = __builtin_bit_cast(v8s, w);
     }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_run = ps[0] + ps[1];
   };
 
-  // MFMA block: PV of the previous tile (if HAS_PV), then S^T of this tile
-  // (if HAS_QK); vst / kst are LDS byte addresses of the V and K tiles
-  auto mfma_block = [&](auto has_pv, auto has_qk, uint32_t vst, uint32_t kst, const v8s* pb,
-                        v16f* sacc) {
-    constexpr bool HPV = decltype(has_pv)::value;
-    constexpr bool HQK = decltype(has_qk)::value;
-    // each section is a scheduling region of its own (the read/MFMA
-    // interleave below is pinned per region)
+  // The MFMA sections.  KOFF is the byte offset in LDS of the K tile the
+  // operands are read from (the V tile follows it); where it is a constant
+  // the per-lane addresses above take it as the reads' immediate offset.  Each
+  // section is a scheduling region of its own (its read/MFMA interleave is
+  // pinned) and runs at raised wave priority, so that while one wave of a
+  // SIMD works through its MFMAs the other wave's softmax arithmetic fills
+  // the issue slots between them.
+  auto qk = [&](int KOFF, v16f* sacc) {
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (HPV) {
-      const char* vs = smem + (vst - smem0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const char* p = vs + v_lane[dc & 3] + 16 * s * RB + 64 * (dc & ~3);
-          const v4s lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(p));
-          const v4s hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(p + 8 * RB));
-          const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dc] = T::mfma32x32x16(av, pb[s], oacc[dc]);
-        }
-      // schedule: 8 reads ahead, then one MFMA per two reads
-      constexpr int NR = 8 * DC, LEAD = 8, MID = (NR - LEAD) / 2;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
+      for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
+    // (reads written out first: the pinned interleave below then applies)
+    v8s kf[2 * KQ];
 #pragma unroll
-      for (int i = 0; i < MID; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DC - MID, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (HQK) {
-      const char* ks = smem + (kst - smem0);
+    for (int kk = 0; kk < KQ; ++kk)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
+        kf[2 * kk + h2] = lds_load16(k_lane[kk] + KOFF + h2 * 32 * RB);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
-      // (reads written out first: the pinned interleave below then applies)
-      v8s kf[2 * KQ];
+    for (int kk = 0; kk < KQ; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk)
+      for (int h2 = 0; h2 < 2; ++h2) sacc[h2] = T::mfma32x32x16(kf[2 * kk + h2], qf[kk], sacc[h2]);
+    // schedule: 6 reads ahead, then one MFMA per read
+    constexpr int NR = 2 * KQ, LEAD = 6;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          kf[2 * kk + h2] = *reinterpret_cast<const v8s*>(ks + k_lane[kk] + h2 * 32 * RB);
-#pragma unroll
-      for (int kk = 0; kk < KQ; ++kk)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) sacc[h2] = T::mfma32x32x16(kf[2 * kk + h2], qf[kk], sacc[h2]);
-      // schedule: 6 reads ahead, then one MFMA per read
-      constexpr int NR = 2 * KQ, LEAD = 6;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
-#pragma unroll
-      for (int i = 0; i < NR - LEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LEAD, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < NR - LEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, LEAD, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto pv = [&](int KOFF, const v8s* pb) {
+    const int VOFF = KOFF + TB;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const uint32_t p = v_lane[dc & 3] + VOFF + 16 * s * RB + 64 * (dc & ~3);
+        const v4s lo = lds_load_tr16(p);
+        const v4s hi = lds_load_tr16(p + 8 * RB);
+        const v8s av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[dc] = T::mfma32x32x16(av, pb[s], oacc[dc]);
+      }
+    // schedule: 8 reads ahead, then one MFMA per two reads
+    constexpr int NR = 8 * DC, LEAD = 8, MID = (NR - LEAD) / 2;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
+#pragma unroll
+    for (int i = 0; i < MID; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DC - MID, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- fp8 cache: widen this wave's RW rows of the staged K and V tiles
@@ -597,17 +662,9 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     lds_barrier();
   };
 
-  // ---- prologue: the first NST - 1 tiles
-  // (t_begin < t_end whenever the tile has a query row: its own key is visible)
-  const int n = t_end - t_begin;
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < n) issue_tile(t_begin + p, id_of(p), p);
-  // the first tile (and Q) landed; the other issued tiles may stay in flight
-  static_assert(NST >= 2 && NST <= 4, "waits assume at most two tiles in flight past the next");
-  if (NST >= 4 && n >= 3) wait_vmcnt<4 * NI>();
-  else if (NST >= 3 && n >= 2) wait_vmcnt<2 * NI>();
-  else wait_vmcnt<0>();
+  // ---- the first tile, the block ids and Q landed
+  wait_vmcnt<0>();
+  claim(ids);
   lds_barrier();
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk) {
@@ -622,42 +679,70 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     if (!row_ok) qf[kk] = z;
   }
 
-  // ---- main loop over key tiles j: tile j + NST - 1 goes into the stage of
-  //      tile j - 1 (all waves passed the barrier after reading it); S^T,
-  //      softmax and PV of tile j; then tile j + 1 must have landed before
-  //      the barrier.
-  int st = 0;  // stage of tile j
-  for (int j = 0; j < n; ++j) {
+  // ---- main loop over key tiles j: tile j + 1 goes into the stage of tile
+  //      j - 1 (all waves passed the barrier after reading it); S^T, softmax
+  //      and PV of tile j; then tile j + 1 must have landed before the
+  //      barrier.  Tile j sits in ring stage j % 2.
+  //
+  //      The tiles are taken in three runs: [0, u0) and [u1, n) may cut a
+  //      row's visible range (the window start, the causal diagonal, the
+  //      sequence end) and run the masked tile code, skipping tiles no row
+  //      of the wave sees; [u0, u1) is visible to every row of the
+  //      workgroup and runs the unmasked code, two tiles per pass, so that
+  //      each tile's stage is a constant.  A wave without query rows (the
+  //      last tile of a sequence) only moves tiles through the ring.
+  static_assert(NST == 2, "the loop alternates two ring stages");
+  auto step = [&](int j, int stage, auto compute_c, auto masked_c) {
     const int tile = t_begin + j;
     const int kbase = tile * kKT;
-    const int pst = st == 0 ? NST - 1 : st - 1;  // stage of tile j - 1
-    if (j + NST - 1 < n) {
-      const int jt = j + NST - 1;
+    if (j + 1 < n) {
+      const int jt = j + 1;
       if ((jt & 63) == 0) {  // next chunk of block ids (every 64 tiles)
         ids = load_ids(t_begin + jt);
         wait_vmcnt<0>();
         claim(ids);
       }
-      issue_tile(tile + NST - 1, id_of(jt), pst);
+      issue_tile(tile + 1, id_of(jt), 1 - stage);
     }
-    const bool act = tile_active(kbase);
-    uint32_t kst = smem0 + st * 2 * TB;
-    if constexpr (F8) {
-      widen(st);
-      kst = smem0 + NST * 2 * TBC;
+    // LDS offset of the K tile the operand reads use (an fp8 stage is first
+    // widened into the tile pair after the ring)
+    const int koff = F8 ? NST * 2 * TBC : stage * 2 * TB;
+    if constexpr (F8) widen(stage);
+    if constexpr (decltype(compute_c)::value) {
+      if (!decltype(masked_c)::value || tile_active(kbase)) {
+        v16f sacc[2];
+        v8s pb[4];
+        qk(koff, sacc);
+        softmax(sacc, kbase, pb, masked_c);
+        pv(koff, pb);
+      }
     }
-    v16f sacc[2];
-    v8s pb[4];
-    if (act) mfma_block(std::false_type{}, std::true_type{}, 0u, kst, pb, sacc);
-    if (act) softmax(sacc, kbase, pb);
-    if (act) mfma_block(std::true_type{}, std::false_type{}, kst + TB, 0u, pb, sacc);
-    // tile j + 1 landed (the tiles issued after it may stay in flight)
-    const int ahead = min(j + NST - 1, n - 1) - (j + 1);
-    if (NST >= 4 && ahead >= 2) wait_vmcnt<4 * NI>();
-    else if (NST >= 3 && ahead == 1) wait_vmcnt<2 * NI>();
-    else wait_vmcnt<0>();
+    // tile j + 1 landed (nothing else is in flight)
+    wait_vmcnt<0>();
     lds_barrier();
-    st = st + 1 == NST ? 0 : st + 1;
+  };
+  if (w_rows) {
+    // unmasked run: every key of the tile is visible to every query row of
+    // the workgroup (positions p_first .. p_last)
+    int u0 = t_begin, u1 = min(t_end, L / kKT);
+    if (a.causal) u1 = min(u1, (p_first + 1) / kKT);
+    if (a.window_left >= 0) {
+      const int64_t lo = static_cast<int64_t>(p_last) - a.window_left;
+      if (lo > 0) u0 = static_cast<int>(max(static_cast<int64_t>(u0), (lo + kKT - 1) / kKT));
+    }
+    u0 = min(u0, t_end) - t_begin;
+    u1 = max(u1 - t_begin, u0);
+    for (int j = 0; j < u0; ++j) step(j, j & 1, std::true_type{}, std::true_type{});
+    int j = u0;
+    if (j < u1 && (j & 1)) step(j++, 1, std::true_type{}, std::false_type{});
+    for (; j + 1 < u1; j += 2) {
+      step(j, 0, std::true_type{}, std::false_type{});
+      step(j + 1, 1, std::true_type{}, std::false_type{});
+    }
+    if (j < u1) step(j++, 0, std::true_type{}, std::false_type{});
+    for (; j < n; ++j) step(j, j & 1, std::true_type{}, std::true_type{});
+  } else {
+    for (int j = 0; j < n; ++j) step(j, j & 1, std::false_type{}, std::false_type{});
   }
 
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
@@ -725,11 +810,12 @@ int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream
   }
   PrefillArgs a = args;
   a.tok_per_tile = kRows<D> / a.G;
-  a.n_qtiles = (max_seqlen_q + a.tok_per_tile - 1) / a.tok_per_tile;
-  if (a.n_qtiles == 0) return 0;
-  // (the API bounds Hkv * max_seqlen_q below 2^31 and B by 65535)
+  if (max_seqlen_q == 0) return 0;
+  // the compact tile list: floor(total_q / tokens per tile) + B slots per
+  // KV head (the API bounds Hkv * (total_q + B) below 2^31)
+  const int64_t slots = a.total_q / a.tok_per_tile + a.B;
   const int splits = a.key_split > 0 ? n_ksplits : 1;
-  const dim3 grid(static_cast<unsigned>(a.Hkv * a.n_qtiles), a.B, static_cast<unsigned>(splits));
+  const dim3 grid(static_cast<unsigned>(a.Hkv * slots), 1, static_cast<unsigned>(splits));
   hipLaunchKernelGGL((prefill_kernel<T, D, FEAT>), grid, dim3(kNW<D> * 64),
                      (prefill_lds_bytes<D, (FEAT & kFp8) != 0>()), stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;

@@ -14,8 +14,9 @@ gfx950 assembly of every prefill instantiation:
    stores or atomics, its write-back or discard): stores and atomics
    (including the decode work counter) are vector-memory instructions.
 
-CPU only: it compiles the kernel source with hipcc (skipped if hipcc is
-missing)."""
+CPU only: it compiles the kernel source with hipcc and the library build's
+flags (skipped if hipcc is missing)."""
+import importlib.util
 import os
 import re
 import shutil
@@ -27,14 +28,23 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "paged_kv_attention_29_amd", "csrc")
 
 
+def _build_flags(src):
+    """The library build's compile flags for one source (its build script,
+    loaded by path: importing the package would load the library)."""
+    spec = importlib.util.spec_from_file_location(
+        "pa_build", os.path.join(ROOT, "paged_kv_attention_29_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [*mod.FLAGS, *mod.EXTRA.get(src, [])]
+
+
 @pytest.fixture(scope="module")
 def prefill_asm(tmp_path_factory):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("isa") / "prefill.s"
-    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S",
+    cmd = [hipcc, *_build_flags("prefill.hip"), "--cuda-device-only", "-S",
            os.path.join(CSRC, "prefill.hip"), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
@@ -113,8 +123,7 @@ def test_no_scalar_cache_writes(src, tmp_path):
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     out = tmp_path / (src + ".s")
-    subprocess.run([hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang",
-                    "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S",
+    subprocess.run([hipcc, *_build_flags(src), "--cuda-device-only", "-S",
                     os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
     bad = [l.strip() for l in out.read_text().split("\n")
            if re.match(r"\s*(s_atomic|s_store|s_buffer_store|s_scratch_store|s_dcache_wb|"
