@@ -408,7 +408,11 @@ int pa_local_virtual_batches(int attn_chunk_size, int block_size,
  *                reads: the first ceil(seq_lens[b] / block_size) of row b
  *                (padding past them is not looked at);
  *     counts[2]  sequences with a negative length, or with more blocks than
- *                a row holds (their rows are not read).
+ *                a row holds (their rows are not read).  A row holds
+ *                block_table_stride entries: the calls take no separate
+ *                count of valid columns, so the stride is the row length
+ *                they may read up to (a caller whose table has fewer valid
+ *                columns than its stride must keep seq_lens within them).
  *   Enqueued on `stream` like the other calls; read counts after it.
  *   block_size a positive multiple of 16; num_blocks > 0.
  */

@@ -24,6 +24,7 @@
 // online-softmax state (fp32, base-2 exponent) and are merged through LDS at
 // the item's end.  The loads of a wave's next step are issued before its
 // current step is computed.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -732,12 +733,18 @@ int launch_h(const DecodeArgs& args, hipStream_t stream) {
   const int64_t items = (int64_t)(args.Hkv / HPW) * args.CG * args.B * args.S;
   const size_t lds = decode_lds_bytes<D, HPW, F8>(args.G);
   if (lds > 65536) {
-    // (the fp8 D = 256 variants with two tiles per step use more than 64 KB)
-    static bool attr_set = false;
-    if (!attr_set) {
-      attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, FEAT, HPW>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(decode_lds_bytes<D, HPW, F8>(16))) == hipSuccess;
+    // (the fp8 D = 256 variants with two tiles per step use more than 64 KB);
+    // raised once per device (the attribute is per device; concurrent first
+    // calls may both set it, which is harmless)
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -3;
+    if (!(attr_set.load() >> dev & 1)) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, FEAT, HPW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(decode_lds_bytes<D, HPW, F8>(16))) != hipSuccess)
+        return -3;
+      attr_set.fetch_or(uint64_t(1) << dev);
     }
   }
   hipLaunchKernelGGL((decode_kernel<T, D, FEAT, HPW>), dim3(static_cast<unsigned>(items)),

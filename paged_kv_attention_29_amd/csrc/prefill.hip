@@ -37,6 +37,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <atomic>
 #include <climits>      // INT_MAX, INT_MIN
 #include <type_traits>  // std::true_type, std::integral_constant
 
@@ -138,6 +139,16 @@ __device__ __forceinline__ int swz_v(int r) {
 // VALU instruction wrote (five); without the first, the DMA can take the
 // previous M0 as its LDS base.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  // Both are wave-uniform; read from lane 0 so that the asm's scalar
+  // operands are scalar registers whatever the register allocator did with
+  // them (free when they already are).  readfirstlane works on int: each
+  // half goes back through uint32_t, so the low half of the address is not
+  // sign-extended into the high one.
+  const uint64_t sb = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb >> 32)));
+  sbase = reinterpret_cast<const void*>(static_cast<uint64_t>(hi) << 32 | lo);
+  lds_base = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_base)));
   uint32_t save;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -801,12 +812,17 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
 
 template <typename T, int D, int FEAT>
 int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    attr_set = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D, FEAT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   static_cast<int>(prefill_lds_bytes<D, (FEAT & kFp8) != 0>())) ==
-               hipSuccess;
+  // the LDS limit of this kernel, raised once per device (the attribute is
+  // per device; concurrent first calls may both set it, which is harmless)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -3;
+  if (!(attr_set.load() >> dev & 1)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D, FEAT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(prefill_lds_bytes<D, (FEAT & kFp8) != 0>())) != hipSuccess)
+      return -3;
+    attr_set.fetch_or(uint64_t(1) << dev);
   }
   PrefillArgs a = args;
   a.tok_per_tile = kRows<D> / a.G;
