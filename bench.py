@@ -153,7 +153,11 @@ class Flush:
         assert rc == 0, rc
 
 
-def run_decode(args, pa, runner, w):
+def run_decode(args, pa, runner, w, merged=True):
+    """The decode step over `layers` caches: reshape_and_cache, then the
+    split decode with its splits merged in the same launch
+    (paged_attn_decode_merged), or (merged=False) paged_attn_decode followed
+    by merge_attn_states."""
     call = w.steps[0].calls[0]
     base = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
     base.fill_context()
@@ -167,7 +171,7 @@ def run_decode(args, pa, runner, w):
     for c in caches:
         c.sinks = bench_sinks(args, w)
     k, v, s = base.step_inputs(w.steps[0])
-    bufs = [c.call_buffers(call, args.splits) for c in caches]
+    bufs = [c.call_buffers(call, args.splits, merged=merged) for c in caches]
     torch.cuda.synchronize()
 
     dec_t, rac_t, merge_t = Timed(), Timed(), Timed()
@@ -179,7 +183,7 @@ def run_decode(args, pa, runner, w):
                 c.write(k, v, s)
         else:
             c.write(k, v, s)
-        if cb.num_splits == 1:
+        if cb.num_splits == 1 or merged:
             if timed:
                 with dec_t:
                     c.run(cb)
@@ -216,7 +220,8 @@ def run_decode(args, pa, runner, w):
     torch.cuda.synchronize()
     nbytes = decode_bytes(w, call, 1 if args.kv_fp8 else 2)
     return dict(ms_per_step=wall_ms, decode_ms=dec_t.median_ms(), decode_min_ms=dec_t.min_ms(),
-                rac_ms=rac_t.median_ms(), merge_ms=merge_t.median_ms(), bytes=nbytes,
+                rac_ms=rac_t.median_ms(),
+                merge_ms=merge_t.median_ms() if merge_t.pairs else 0.0, bytes=nbytes,
                 tokens=int(s.numel()))
 
 
@@ -308,25 +313,30 @@ def fill_cache_on_gpu(cache, seed: int):
 
 
 def run_decode_call(args, pa, runner, flush, w, call_index=0):
-    """Split decode + merge of one decode call with the scratch write
-    between repetitions: kernel and whole-call times (median, min)."""
+    """One decode call (splits merged in the launch, or with --merge separate
+    a split decode then merge_attn_states) with the scratch read between
+    repetitions: kernel and whole-call times (median, min)."""
     call = w.steps[0].calls[call_index]
     cache = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
     fill_cache_on_gpu(cache, seed=w.seed)
     cache.sinks = bench_sinks(args, w)
-    cb = cache.call_buffers(call)
+    merged = args.merge == "merged"
+    cb = cache.call_buffers(call, merged=merged)
     S = cb.num_splits
     dec_t, mer_t, all_t = Timed(), Timed(), Timed()
 
     def decode():
-        pa.paged_attn_decode(None if S > 1 else cb.out, cb.q, cache.key_cache, cache.value_cache,
+        if merged or S == 1:
+            cache.run(cb)
+            return
+        pa.paged_attn_decode(None, cb.q, cache.key_cache, cache.value_cache,
                              cb.seq_lens, cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
                              w.softcap, cache.alibi, S, part_out=cb.part_out,
-                             part_lse=cb.part_lse, lse=None if S > 1 else cb.lse,
-                             sinks=cache.sinks, k_scale=cache.k_scale, v_scale=cache.v_scale)
+                             part_lse=cb.part_lse, sinks=cache.sinks, k_scale=cache.k_scale,
+                             v_scale=cache.v_scale)
 
     def merge():
-        if S > 1:
+        if S > 1 and not merged:
             pa.merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse)
 
     for _ in range(args.warmup):
@@ -347,6 +357,7 @@ def run_decode_call(args, pa, runner, flush, w, call_index=0):
     digest = source_digest("decode.hip", "common.h")
     return {
         "workload": w.name + ("_kvfp8" if args.kv_fp8 else ""), "num_splits": S,
+        "splits_merged_in_kernel": merged and S > 1,
         "bytes": nbytes, "decode_ms": round(dec_t.median_ms(), 4),
         "decode_min_ms": round(dec_t.min_ms(), 4), "merge_ms": round(mer_t.median_ms(), 4),
         "call_ms": round(all_t.median_ms(), 4), "reps": len(dec_t.pairs),
@@ -355,7 +366,7 @@ def run_decode_call(args, pa, runner, flush, w, call_index=0):
                      "unit": "GB/s", "frac": round(kern / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(
                          f"decode:{w.name}{'_kvfp8' if args.kv_fp8 else ''}:S{S}", digest),
-                     "kernel": "paged_attn_decode"},
+                     "kernel": "paged_attn_decode_merged" if merged and S > 1 else "paged_attn_decode"},
     }
 
 
@@ -639,6 +650,9 @@ def main():
                     help="decode/mixed/long: pass per-head attention-sink logits")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="decode/mixed/long: fp8 (e4m3) K/V cache with per-tensor scales")
+    ap.add_argument("--merge", choices=["merged", "separate"], default="separate",
+                    help="split decode: decode then merge_attn_states (the faster on MI355X), "
+                         "or the splits merged in the decode launch (paged_attn_decode_merged)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -678,7 +692,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    r = run_decode(args, pa, runner, w)
+    merged = args.merge == "merged" and args.splits > 1
+    r = run_decode(args, pa, runner, w, merged=merged)
     gbs = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
     kern_gbs = r["bytes"] / (r["decode_ms"] * 1e-3) / 1e9
     digest = source_digest("decode.hip", "common.h")
@@ -693,11 +708,14 @@ def main():
                    "context_tokens": int(call.seq_lens.sum()), "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
                    "block_size": w.block_size, "num_splits": args.splits,
-                   "layers": args.layers, "step": "reshape_and_cache + decode + merge",
+                   "layers": args.layers,
+                   "step": ("reshape_and_cache + decode with the splits merged in the launch"
+                            if merged else "reshape_and_cache + decode + merge"),
                    "attention_sinks": bool(args.sinks)},
         "kernels_ms": {"reshape_and_cache": round(r["rac_ms"], 4),
-                       "paged_attn_decode": round(r["decode_ms"], 4),
-                       "paged_attn_decode_min": round(r["decode_min_ms"], 4),
+                       ("paged_attn_decode_merged" if merged else "paged_attn_decode"):
+                           round(r["decode_ms"], 4),
+                       "decode_min": round(r["decode_min_ms"], 4),
                        "merge_attn_states": round(r["merge_ms"], 4),
                        "statistic": f"median over {args.steps} launches (HIP events)"},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -705,8 +723,16 @@ def main():
                      "traffic": traffic_from_profile(
                          f"decode:{w.name}{'_kvfp8' if args.kv_fp8 else ''}:S{args.splits}",
                          digest),
-                     "kernel": "paged_attn_decode", "bytes_per_launch": r["bytes"]},
+                     "kernel": "paged_attn_decode_merged" if merged else "paged_attn_decode",
+                     "bytes_per_launch": r["bytes"]},
     }
+    if args.splits > 1 and not args.no_extra:
+        # the same step with the other way of merging the splits
+        rs = run_decode(args, pa, runner, w, merged=not merged)
+        out["merged_in_kernel" if not merged else "separate_merge"] = {
+            "ms_per_step": round(rs["ms_per_step"], 4),
+            "GB/s": round(rs["bytes"] / (rs["ms_per_step"] * 1e-3) / 1e9, 1),
+            "decode_ms": round(rs["decode_ms"], 4), "merge_ms": round(rs["merge_ms"], 4)}
     flush = Flush(pa)
     if not args.no_prefill and args.workload == "decode":
         out["prefill"] = run_prefill(args, pa, runner, flush)

@@ -211,6 +211,43 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse,
                       const float* v_scale, const float* q_scale, void* stream);
 
 /*
+ * paged_attn_decode_merged — paged_attn_decode with the splits merged
+ * inside the same launch: out [num_seqs, num_heads, head_size] (dtype) and,
+ * if lse != NULL, lse fp32 [num_heads, num_seqs] receive what
+ * paged_attn_decode followed by merge_attn_states(out, lse, part_out,
+ * part_lse, num_splits, ...) gives, the same arithmetic in the same order
+ * [vLLM flash_attn.py (e2f56c3), FlashAttentionMetadataBuilder, the
+ * split-KV intermediates; merge_attn_states].  Every split writes its
+ * partial result to part_out / part_lse (as paged_attn_decode, except
+ * that splits without visible keys write nothing); the split of a
+ * (sequence, group of query heads) that finishes last merges the partials
+ * of its group, counting arrivals in split_counters.
+ *
+ *   split_counters  int32 [num_seqs * num_heads], device, caller-owned
+ *                   workspace that must be all zero on entry (e.g. once,
+ *                   after allocation); every call leaves it all zero.
+ *                   Calls that overlap on one counters array race.
+ *   part_out, part_lse as for paged_attn_decode (overwritten workspace).
+ *   num_splits == 1: the plain single-pass decode (the workspaces are not
+ *   used and may be NULL).  Other arguments and errors as paged_attn_decode.
+ *   One launch instead of two; every split item then waits for its
+ *   device-coherent partial stores and its count before it ends, which on
+ *   MI355X costs more than the separate merge launch for a 64-sequence,
+ *   8-split batch (145 us against 130 + 6 us).
+ */
+int paged_attn_decode_merged(void* out, float* lse, float* part_out, float* part_lse,
+                             int32_t* split_counters, const void* q,
+                             const void* key_cache, const void* value_cache,
+                             const int32_t* seq_lens, const int32_t* block_table,
+                             int64_t block_table_stride, int num_seqs, int max_seq_len,
+                             int num_heads, int num_kv_heads, int head_size, int block_size,
+                             int64_t num_blocks, float scale, int window_left, float softcap,
+                             const float* alibi_slopes, const float* sinks, int num_splits,
+                             pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
+                             const float* k_scale, const float* v_scale,
+                             const float* q_scale, void* stream);
+
+/*
  * paged_attn_decode_noalloc — for callers that cannot allocate device
  * memory (code under graph capture, tight serving loops, harnesses that
  * forbid allocation): paged_attn_decode with num_splits parts followed by

@@ -28,6 +28,7 @@ __all__ = [
     "reshape_and_cache",
     "paged_attn_prefill",
     "paged_attn_decode",
+    "paged_attn_decode_merged",
     "paged_attn_decode_noalloc",
     "merge_attn_states",
     "scaled_fp8_quant",
@@ -67,6 +68,10 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
                                       _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.paged_attn_decode_merged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                                             _i32, _f32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
+                                             _vp]
     lib.paged_attn_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i64, _f32, _i32, _f32, _vp,
                                               _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
@@ -302,6 +307,47 @@ def _attn_dtype(q, out, out_dtype):
     if q.dtype in _ATTN:
         return q.dtype
     raise TypeError("an fp8 query without out needs out_dtype")
+
+
+def paged_attn_decode_merged(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, seq_lens: torch.Tensor,
+                             block_table: torch.Tensor, max_seq_len: int, scale: float,
+                             num_splits: int, part_out: Optional[torch.Tensor],
+                             part_lse: Optional[torch.Tensor],
+                             split_counters: Optional[torch.Tensor],
+                             window_left: int = -1, softcap: float = 0.0,
+                             alibi_slopes: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None, stream=None,
+                             sinks: Optional[torch.Tensor] = None,
+                             k_scale: Optional[torch.Tensor] = None,
+                             v_scale: Optional[torch.Tensor] = None,
+                             q_scale: Optional[torch.Tensor] = None) -> None:
+    """Split decode whose splits are merged in the same launch; out receives
+    the merged result.  split_counters: int32 with at least num_seqs *
+    num_heads elements, all zero on entry (left zero)."""
+    _need("out", out, _ATTN, contiguous=True)
+    _need_q(q, out, q_scale)
+    _need_cache(key_cache, value_cache)
+    _need("seq_lens", seq_lens, _INT32, contiguous=True)
+    _need_table(block_table)
+    _need("lse", lse, _F32, contiguous=True, optional=True)
+    _need("part_out", part_out, _F32, contiguous=True, optional=num_splits <= 1)
+    _need("part_lse", part_lse, _F32, contiguous=True, optional=num_splits <= 1)
+    _need("split_counters", split_counters, _INT32, contiguous=True, optional=num_splits <= 1)
+    _need("alibi_slopes", alibi_slopes, _F32, contiguous=True, optional=True)
+    _need("sinks", sinks, _F32, contiguous=True, optional=True)
+    _need_scales(k_scale, v_scale)
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = key_cache.shape
+    if split_counters is not None and split_counters.numel() < b * hq:
+        raise ValueError("split_counters needs num_seqs * num_heads elements")
+    _check("paged_attn_decode_merged", lib.paged_attn_decode_merged(
+        _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse), _ptr(split_counters), _ptr(q),
+        _ptr(key_cache), _ptr(value_cache), _ptr(seq_lens), _ptr(block_table),
+        block_table.stride(0), b, int(max_seq_len), hq, hkv, d, bs, nb, float(scale),
+        int(window_left), float(softcap), _ptr(alibi_slopes), _ptr(sinks), int(num_splits),
+        _code(out.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _ptr(q_scale),
+        _stream(stream)))
 
 
 def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,

@@ -320,6 +320,36 @@ int paged_attn_decode(void* out, float* lse, float* part_out, float* part_lse, c
   return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
 }
 
+int paged_attn_decode_merged(void* out, float* lse, float* part_out, float* part_lse,
+                             int32_t* split_counters, const void* q, const void* key_cache,
+                             const void* value_cache, const int32_t* seq_lens,
+                             const int32_t* block_table, int64_t block_table_stride, int num_seqs,
+                             int max_seq_len, int num_heads, int num_kv_heads, int head_size,
+                             int block_size, int64_t num_blocks, float scale, int window_left,
+                             float softcap, const float* alibi_slopes, const float* sinks,
+                             int num_splits, pa_dtype_t dtype, pa_dtype_t kv_cache_dtype,
+                             const float* k_scale, const float* v_scale, const float* q_scale,
+                             void* stream) {
+  const char* fn = "paged_attn_decode_merged";
+  int rc = check_decode(fn, num_seqs, max_seq_len, num_heads, num_kv_heads, head_size, block_size,
+                        num_blocks, scale, window_left, softcap, num_splits, dtype,
+                        kv_cache_dtype, k_scale, v_scale, q_scale, q, key_cache, value_cache,
+                        seq_lens, block_table, block_table_stride);
+  if (rc != PA_OK) return rc;
+  if (out == nullptr) return fail(PA_ERR_INVALID, "%s: output buffer must be provided", fn);
+  if (num_splits > 1 && (part_out == nullptr || part_lse == nullptr || split_counters == nullptr))
+    return fail(PA_ERR_INVALID, "%s: num_splits > 1 needs part_out, part_lse and split_counters",
+                fn);
+  if (num_seqs == 0) return ok();
+  pa::AttnParams p = decode_params(out, lse, part_out, part_lse, q, key_cache, value_cache,
+                                   seq_lens, block_table, block_table_stride, num_seqs,
+                                   max_seq_len, num_heads, num_kv_heads, head_size, block_size,
+                                   scale, window_left, softcap, alibi_slopes, sinks, num_splits,
+                                   dtype, kv_cache_dtype, k_scale, v_scale, q_scale);
+  p.split_counters = split_counters;
+  return hip_result(pa::launch_decode(p, static_cast<hipStream_t>(stream)), fn);
+}
+
 int paged_attn_decode_noalloc(void* out, float* lse, const void* q, const void* key_cache,
                               const void* value_cache, const int32_t* seq_lens,
                               const int32_t* block_table, int64_t block_table_stride,

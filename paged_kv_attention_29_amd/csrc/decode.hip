@@ -68,6 +68,11 @@ struct DecodeArgs {
   // fp8 query (with an fp8 cache): q holds e4m3 codes and this device fp32
   // scalar is their descale; null for a 16-bit query
   const float* q_scale;
+  // merged splits (S > 1): one int counter per (sequence, column group),
+  // zero on entry and left zero; the last split item of a (sequence, column
+  // group) to finish merges the partial results into out / lse.  Null: the
+  // partials are the result.
+  int* counters;
 };
 
 enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4, kQ8 = 8 };
@@ -247,6 +252,9 @@ __device__ void ranked_item_wave0(const DecodeArgs& a, int* sh, int* res) {
 // The pieces of one work item.
 template <typename T, int D, int FEAT, int HPW>
 struct Dec {
+  using TT = T;
+  static constexpr int kD = D;
+  static constexpr int kHPW = HPW;
   static constexpr bool SOFTCAP = FEAT & kSoftcap;
   static constexpr bool ALIBI = FEAT & kAlibi;
   static constexpr bool F8 = FEAT & kFp8;
@@ -555,7 +563,16 @@ struct Dec {
   static __device__ __forceinline__ void emit4(const DecodeArgs& a, int hb, int b, int split,
                                                int j, int d, v4f val, float lse) {
     const int h = hb + j;
-    if (a.S > 1) {
+    if (a.S > 1 && a.counters != nullptr) {
+      // merged splits: device-coherent stores (another XCD's workgroup may
+      // merge them), so no L2-wide write-back is needed before the count
+      float* po = a.part_out + (((int64_t)split * a.B + b) * a.Hq + h) * D + d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) __hip_atomic_store(po + e, val[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0)
+        __hip_atomic_store(a.part_lse + ((int64_t)split * a.Hq + h) * a.B + b, lse, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if (a.S > 1) {
       *reinterpret_cast<v4f*>(a.part_out + (((int64_t)split * a.B + b) * a.Hq + h) * D + d) = val;
       if (d == 0) a.part_lse[((int64_t)split * a.Hq + h) * a.B + b] = lse;
     } else {
@@ -630,6 +647,118 @@ struct Dec {
 };
 
 // ---------------------------------------------------------------------------
+// Merged splits.  A split item's partial result goes to part_out / part_lse
+// as without merging; then the item counts itself in its (sequence, column
+// group) counter, and the item that brings the count to the number of
+// partials the group has merges them all into out / lse and resets the
+// counter.  The partials of a group are those of its splits with visible
+// keys, plus split 0's when it has none but holds the sinks (its partial is
+// the sink alone); a sequence with neither has its zero / -inf result
+// written by split 0 directly.  The merge is merge_attn_states's arithmetic
+// in its order (parts 0, 1, ...), the absent parts weighing 0.
+template <typename K>
+__device__ __forceinline__ void merged_tail(const DecodeArgs& a, const typename K::Item& it,
+                                            int grp, int L, bool wrote, int* flag) {
+  constexpr int D = K::kD;
+  const bool sinks = a.sinks != nullptr;
+  int pf = 0, pl = -1;  // splits with visible keys
+  if (L > 0) split_span(a, L, pf, pl);
+  const bool sink_part = sinks && (L <= 0 || pf > 0);  // split 0: the sink alone
+  const int parts = (pl - pf + 1) + (sink_part ? 1 : 0);
+  auto written = [&](int p) { return (p >= pf && p <= pl) || (p == 0 && sink_part); };
+  const int64_t B = a.B;
+  if (parts == 0) {
+    // no partial at all: split 0 writes the empty result
+    if (it.split != 0) return;
+    for (int idx = threadIdx.x; idx < it.nc * (D / 4); idx += kWaves * 64) {
+      const int j = idx / (D / 4);
+      const int d = (idx - j * (D / 4)) * 4;
+      const int h = it.hb + j;
+      uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)it.b * a.Hq + h) * D + d;
+      *reinterpret_cast<u32x2*>(o) = u32x2{0u, 0u};
+      if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * B + it.b] = kNegInf;
+    }
+    return;
+  }
+  if (!wrote) return;
+  // The partials were stored device-coherent (emit4); waiting for them here
+  // puts them at the device's coherence point before the count.  (A fence
+  // at agent scope would write back and invalidate the whole L2 of the
+  // XCD, for every item.)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* cnt = a.counters + (int64_t)it.b * (a.Hkv / K::kHPW * a.CG) + grp;
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == parts - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  // the other items' partials: device-coherent loads, issued after the
+  // count showed that every one of them was stored
+  for (int idx = threadIdx.x; idx < it.nc * (D / 4); idx += kWaves * 64) {
+    const int j = idx / (D / 4);
+    const int d = (idx - j * (D / 4)) * 4;
+    const int h = it.hb + j;
+    // parts in batches of 8 whose loads go out together (device-coherent
+    // loads: issued after the count showed every part stored)
+    constexpr int NB = 8;
+    float l[NB];
+    v4f x[NB];
+    auto load_batch = [&](int p0, bool rows) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int p = p0 + i;
+        const bool ok = p < a.S && written(p);
+        l[i] = ok ? __hip_atomic_load(a.part_lse + ((int64_t)p * a.Hq + h) * B + it.b,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : kNegInf;
+        if (rows) {
+          const float* px = a.part_out + (((int64_t)p * B + it.b) * a.Hq + h) * D + d;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[i][e] = ok ? __hip_atomic_load(px + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+        }
+      }
+    };
+    // the maximum log-sum-exp (with at most 8 parts the first batch's rows
+    // are loaded along with it and kept)
+    float m = kNegInf;
+    for (int p0 = 0; p0 < a.S; p0 += NB) {
+      load_batch(p0, a.S <= NB);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) m = fmaxf(m, l[i]);
+    }
+    uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)it.b * a.Hq + h) * D + d;
+    if (m == kNegInf) {
+      *reinterpret_cast<u32x2*>(o) = u32x2{0u, 0u};
+      if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * B + it.b] = kNegInf;
+      continue;
+    }
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int p0 = 0; p0 < a.S; p0 += NB) {
+      if (a.S > NB) load_batch(p0, true);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        // parts in order; an absent part weighs 0
+        const float w = l[i] == kNegInf ? 0.f : fast_exp2((l[i] - m) * kLog2e);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = w != 0.0f ? __builtin_fmaf(w, x[i][e], acc[e]) : acc[e];
+      }
+    }
+    const float inv = 1.0f / wsum;
+    const uint32_t lo = K::TT::from_float(acc[0] * inv) | static_cast<uint32_t>(K::TT::from_float(acc[1] * inv)) << 16;
+    const uint32_t hi = K::TT::from_float(acc[2] * inv) | static_cast<uint32_t>(K::TT::from_float(acc[3] * inv)) << 16;
+    *reinterpret_cast<u32x2*>(o) = u32x2{lo, hi};
+    if (d == 0 && a.lse != nullptr) a.lse[(int64_t)h * B + it.b] = m + __logf(wsum);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One work item per workgroup.
 // Item order: split-major; within split p the (KV-head group, sequence) pairs
 // are rotated by p groups.  Workgroup i runs on XCD i % 8 and, within it, on
@@ -680,8 +809,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   }
 
   const typename K::Item it = K::make_item(a, grp, b, split, L);
+  int* const flag = reinterpret_cast<int*>(smem + rank_slot_offset<D, HPW, K::F8>(a.G));
   if (it.lo_vis >= it.hi) {
-    K::emit_empty(a, it);
+    // (merged: only split 0 of a group holding the sinks writes a partial)
+    const bool write = a.counters == nullptr || (split == 0 && a.sinks != nullptr);
+    if (write) K::emit_empty(a, it);
+    if (a.counters != nullptr) merged_tail<K>(a, it, grp, L, write, flag);
     return;
   }
   const bool col_ok = r16 < it.nc;
@@ -725,6 +858,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
     cur = nxt;
   }
   K::combine_emit(a, it, wave, r16, c4, m_run, l_run, o, reinterpret_cast<float*>(smem));
+  if (a.counters != nullptr) merged_tail<K>(a, it, grp, L, true, flag);
 }
 
 template <typename T, int D, int FEAT, int HPW>
@@ -815,6 +949,7 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.k_scale = p.k_scale;
   a.v_scale = p.v_scale;
   a.q_scale = p.q_scale;
+  a.counters = p.num_splits > 1 ? p.split_counters : nullptr;
   const bool alibi = p.alibi_slopes != nullptr;
   if (p.kv_fp8 && p.q_scale != nullptr) {
     if (p.dtype == kBF16) return launch_t<BF16, kFp8 | kQ8>(a, p.head_size, softcap, alibi, stream);

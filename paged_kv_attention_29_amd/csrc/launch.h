@@ -59,6 +59,10 @@ struct AttnParams {
   const float* k_scale;  // fp8 cache: device fp32 scales
   const float* v_scale;
   const float* q_scale;  // non-null: q holds fp8 (e4m3) codes and this is their descale
+  // decode with num_splits > 1: non-null merges the splits in the kernel
+  // (one int per (sequence, query head), zero on entry, left zero) and
+  // writes out / lse; null writes the partials only
+  int32_t* split_counters = nullptr;
   int num_splits;
   int key_split;  // prefill only: keys per split (a multiple of 64), 0 = none
   Dtype dtype;

@@ -96,9 +96,10 @@ __global__ __launch_bounds__(256) void merge_kernel(void* __restrict__ out,
       if (j < nb0) {
         const float w = weight(j);
         wsum += w;
-        // an empty part (w = 0) may hold anything, finite or not
+        // an empty part (w = 0) may hold anything, finite or not; each part
+        // adds w * x with one fused multiply-add
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += w != 0.0f ? w * x0[j][e] : 0.0f;
+        for (int e = 0; e < EPL; ++e) acc[e] = w != 0.0f ? __builtin_fmaf(w, x0[j][e], acc[e]) : acc[e];
       }
     // the other parts in batches of 8: the loads of a batch are independent
     // and go out together
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void merge_kernel(void* __restrict__ out,
       for (int j = 0; j < 8; ++j) {
         wsum += w[j];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += w[j] != 0.0f ? w[j] * x[j][e] : 0.0f;
+        for (int e = 0; e < EPL; ++e) acc[e] = w[j] != 0.0f ? __builtin_fmaf(w[j], x[j][e], acc[e]) : acc[e];
       }
     }
     for (; p < S; ++p) {
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void merge_kernel(void* __restrict__ out,
       wsum += w;
       if (w == 0.0f) continue;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += w * Elem<PT>::ld(parts, p * part_stride + row + e);
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, Elem<PT>::ld(parts, p * part_stride + row + e), acc[e]);
     }
   };
   if (S <= 64) accumulate(std::true_type{});

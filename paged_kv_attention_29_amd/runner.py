@@ -14,7 +14,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import (merge_attn_states, paged_attn_decode, paged_attn_prefill, reshape_and_cache)
+from . import (merge_attn_states, paged_attn_decode, paged_attn_decode_merged, paged_attn_prefill,
+               reshape_and_cache)
 
 
 @dataclass
@@ -33,6 +34,9 @@ class CallBuffers:
     part_out: Optional[torch.Tensor] = None
     part_lse: Optional[torch.Tensor] = None
     causal: bool = True
+    # split decode merged in the decode launch (paged_attn_decode_merged):
+    # its zeroed counters; None runs decode then merge_attn_states
+    split_counters: Optional[torch.Tensor] = None
 
 
 class PagedCache:
@@ -72,7 +76,8 @@ class PagedCache:
         k, v, s = self.w.step_tokens(step)
         return k.to(self.device), v.to(self.device), s.to(self.device)
 
-    def call_buffers(self, call, num_splits: Optional[int] = None) -> CallBuffers:
+    def call_buffers(self, call, num_splits: Optional[int] = None,
+                     merged: bool = False) -> CallBuffers:
         w, dev = self.w, self.device
         S = call.num_splits if num_splits is None else num_splits
         T = call.q.shape[0]
@@ -82,6 +87,9 @@ class PagedCache:
         if call.kind == "decode" and S > 1:
             po = torch.empty(S, T, w.num_heads, w.head_size, dtype=torch.float32, device=dev)
             pl = torch.empty(S, w.num_heads, T, dtype=torch.float32, device=dev)
+        cnt = None
+        if call.kind == "decode" and S > 1 and merged:
+            cnt = torch.zeros(T * w.num_heads, dtype=torch.int32, device=dev)
         ids = torch.from_numpy(np.asarray(call.seq_ids, dtype=np.int64)).to(dev)
         return CallBuffers(
             kind=call.kind, q=call.q.to(dev),
@@ -89,7 +97,8 @@ class PagedCache:
             seq_lens=torch.from_numpy(call.seq_lens.astype(np.int32)).to(dev),
             block_table=self.block_table.index_select(0, ids).contiguous(),
             max_seqlen_q=int(call.query_lens.max()), max_seqlen_k=int(call.seq_lens.max()),
-            num_splits=S, out=out, lse=lse, part_out=po, part_lse=pl, causal=bool(call.causal))
+            num_splits=S, out=out, lse=lse, part_out=po, part_lse=pl, causal=bool(call.causal),
+            split_counters=cnt)
 
     def run(self, cb: CallBuffers, stream=None) -> None:
         w = self.w
@@ -104,6 +113,12 @@ class PagedCache:
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
                               self.alibi, 1, lse=cb.lse, stream=stream, sinks=self.sinks,
                               k_scale=self.k_scale, v_scale=self.v_scale)
+        elif cb.split_counters is not None:
+            paged_attn_decode_merged(cb.out, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
+                                     cb.block_table, cb.max_seqlen_k, w.scale, cb.num_splits,
+                                     cb.part_out, cb.part_lse, cb.split_counters, w.window_left,
+                                     w.softcap, self.alibi, lse=cb.lse, stream=stream,
+                                     sinks=self.sinks, k_scale=self.k_scale, v_scale=self.v_scale)
         else:
             paged_attn_decode(None, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,

@@ -288,3 +288,23 @@ def test_binding_rejects_bad_prefill_and_cache_tensors(lib):
         lib.paged_attn_decode(None, g(2, 4, 64), *cache, g(2, dt=torch.int32),
                               g(2, 4, dt=torch.int32), 10, 0.125, num_splits=2,
                               part_out=g(2, 2, 4, 64), part_lse=g(2, 4, 2, dt=torch.float32))
+
+
+def test_binding_merged_decode_guards(lib):
+    """paged_attn_decode_merged: with splits it needs int32 counters of at
+    least num_seqs * num_heads elements (checked before the C call)."""
+    import torch
+    a = _decode_args(torch)
+    out, q, kc, vc, sl, bt = (a.pop(k) for k in ("out", "q", "key_cache", "value_cache",
+                                                 "seq_lens", "block_table"))
+    po = _as_gpu(torch.zeros(4, 2, 4, 64, dtype=torch.float32))
+    pl = _as_gpu(torch.zeros(4, 4, 2, dtype=torch.float32))
+    with pytest.raises(TypeError, match="required"):   # missing counters
+        lib.paged_attn_decode_merged(out, q, kc, vc, sl, bt, a["max_seq_len"], a["scale"], 4,
+                                     po, pl, None)
+    with pytest.raises(TypeError):    # int64 counters
+        lib.paged_attn_decode_merged(out, q, kc, vc, sl, bt, a["max_seq_len"], a["scale"], 4,
+                                     po, pl, _as_gpu(torch.zeros(8, dtype=torch.int64)))
+    with pytest.raises(ValueError, match="num_seqs \\* num_heads"):  # too few
+        lib.paged_attn_decode_merged(out, q, kc, vc, sl, bt, a["max_seq_len"], a["scale"], 4,
+                                     po, pl, _as_gpu(torch.zeros(7, dtype=torch.int32)))
