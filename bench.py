@@ -56,6 +56,14 @@ def visible_keys(L: int, pos: int, causal: bool, window_left: int) -> int:
 # per-tensor scales of the fp8 (e4m3) cache in --kv-fp8 runs: the largest
 # |x| of N(0,1) data over a few million draws (about 5.6) maps to 448
 FP8_SCALES = (5.6 / 448.0, 5.6 / 448.0)
+# --kv-fp8 quantises the query too (per-tensor scale, scaled_fp8_quant), the
+# pages' default fp8 flow; --fp8-q16 keeps the 16-bit query
+Q_FP8_SCALE = 5.6 / 448.0
+
+
+def set_fp8_query(args, cache):
+    if args.kv_fp8 and not args.fp8_q16:
+        cache.q_scale = torch.tensor([Q_FP8_SCALE], dtype=torch.float32, device="cuda")
 
 
 def decode_bytes(w, call, elem: int = 2) -> int:
@@ -160,6 +168,7 @@ def run_decode(args, pa, runner, w, merged=True):
     by merge_attn_states."""
     call = w.steps[0].calls[0]
     base = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
+    set_fp8_query(args, base)
     base.fill_context()
     caches = [base]
     for _ in range(args.layers - 1):
@@ -191,7 +200,7 @@ def run_decode(args, pa, runner, w, merged=True):
                 c.run(cb)
             return
         kw = dict(part_out=cb.part_out, part_lse=cb.part_lse, k_scale=c.k_scale,
-                  v_scale=c.v_scale)
+                  v_scale=c.v_scale, q_scale=c.q_scale, out_dtype=w.dtype)
         if timed:
             with dec_t:
                 pa.paged_attn_decode(None, cb.q, c.key_cache, c.value_cache, cb.seq_lens,
@@ -225,6 +234,12 @@ def run_decode(args, pa, runner, w, merged=True):
                 tokens=int(s.numel()))
 
 
+def fp8_suffix(args):
+    if not args.kv_fp8:
+        return ""
+    return "_kvfp8" if args.fp8_q16 else "_kvfp8_qfp8"
+
+
 def bench_sinks(args, w):
     """--sinks: seeded fp32 attention-sink logits, one per query head."""
     if not args.sinks:
@@ -252,6 +267,7 @@ def run_prefill(args, pa, runner, flush, w=None, call_index=0, write=True):
     w = W.prefill_batch() if w is None else w
     call = w.steps[0].calls[call_index]
     cache = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
+    set_fp8_query(args, cache)
     if any(int(c) > 0 for c in w.context_lens):
         fill_cache_on_gpu(cache, seed=w.seed)
     cache.sinks = bench_sinks(args, w)
@@ -279,12 +295,12 @@ def run_prefill(args, pa, runner, flush, w=None, call_index=0, write=True):
     key = "prefill" + ("" if w.name.startswith("prefill") else ":" + w.name)
     out = {
         "value": round(tflops, 2), "unit": "TFLOP/s",
-        "workload": w.name + ("_kvfp8" if args.kv_fp8 else ""),
+        "workload": w.name + fp8_suffix(args),
         "ms_per_call": round(ms, 4), "min_ms": round(pre_t.min_ms(), 4),
         "reps": len(pre_t.pairs), "flops": flops, "query_tokens": int(call.q.shape[0]),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile(key + ("_kvfp8" if args.kv_fp8 else ""),
+                     "traffic": traffic_from_profile(key + fp8_suffix(args),
                                                      digest)},
     }
     if write:
@@ -318,6 +334,7 @@ def run_decode_call(args, pa, runner, flush, w, call_index=0):
     repetitions: kernel and whole-call times (median, min)."""
     call = w.steps[0].calls[call_index]
     cache = runner.PagedCache(w, kv_scales=FP8_SCALES if args.kv_fp8 else None)
+    set_fp8_query(args, cache)
     fill_cache_on_gpu(cache, seed=w.seed)
     cache.sinks = bench_sinks(args, w)
     merged = args.merge == "merged"
@@ -333,7 +350,7 @@ def run_decode_call(args, pa, runner, flush, w, call_index=0):
                              cb.seq_lens, cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
                              w.softcap, cache.alibi, S, part_out=cb.part_out,
                              part_lse=cb.part_lse, sinks=cache.sinks, k_scale=cache.k_scale,
-                             v_scale=cache.v_scale)
+                             v_scale=cache.v_scale, q_scale=cache.q_scale, out_dtype=w.dtype)
 
     def merge():
         if S > 1 and not merged:
@@ -356,7 +373,7 @@ def run_decode_call(args, pa, runner, flush, w, call_index=0):
     whole = nbytes / (all_t.median_ms() * 1e-3) / 1e9
     digest = source_digest("decode.hip", "common.h")
     return {
-        "workload": w.name + ("_kvfp8" if args.kv_fp8 else ""), "num_splits": S,
+        "workload": w.name + fp8_suffix(args), "num_splits": S,
         "splits_merged_in_kernel": merged and S > 1,
         "bytes": nbytes, "decode_ms": round(dec_t.median_ms(), 4),
         "decode_min_ms": round(dec_t.min_ms(), 4), "merge_ms": round(mer_t.median_ms(), 4),
@@ -365,7 +382,7 @@ def run_decode_call(args, pa, runner, flush, w, call_index=0):
         "roofline": {"bound": "hbm", "achieved": round(kern, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(
-                         f"decode:{w.name}{'_kvfp8' if args.kv_fp8 else ''}:S{S}", digest),
+                         f"decode:{w.name}{fp8_suffix(args)}:S{S}", digest),
                      "kernel": "paged_attn_decode_merged" if merged and S > 1 else "paged_attn_decode"},
     }
 
@@ -650,6 +667,8 @@ def main():
                     help="decode/mixed/long: pass per-head attention-sink logits")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="decode/mixed/long: fp8 (e4m3) K/V cache with per-tensor scales")
+    ap.add_argument("--fp8-q16", action="store_true",
+                    help="with --kv-fp8: keep the query in 16 bits (not quantised)")
     ap.add_argument("--merge", choices=["merged", "separate"], default="separate",
                     help="split decode: decode then merge_attn_states (the faster on MI355X), "
                          "or the splits merged in the decode launch (paged_attn_decode_merged)")
@@ -701,9 +720,10 @@ def main():
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3 K/V cache, bf16 q" if args.kv_fp8 else "bf16",
+        "dtype": (("fp8_e4m3 K/V cache, bf16 q" if args.fp8_q16 else "fp8_e4m3 K/V cache and q")
+                  if args.kv_fp8 else "bf16"),
         "data": "synthetic",
-        "config": {"workload": w.name + ("_kvfp8" if args.kv_fp8 else ""),
+        "config": {"workload": w.name + fp8_suffix(args),
                    "num_seqs": call.num_seqs,
                    "context_tokens": int(call.seq_lens.sum()), "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
@@ -721,7 +741,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(
-                         f"decode:{w.name}{'_kvfp8' if args.kv_fp8 else ''}:S{args.splits}",
+                         f"decode:{w.name}{fp8_suffix(args)}:S{args.splits}",
                          digest),
                      "kernel": "paged_attn_decode_merged" if merged else "paged_attn_decode",
                      "bytes_per_launch": r["bytes"]},

@@ -127,6 +127,17 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
 }
 
+// fp8 K rows (D bytes) read as the fp8 MFMA's A operand: 16 consecutive
+// rows at one 16-byte piece index per 16 lanes must cover all 64 banks,
+// i.e. 256 / D rows share a bank line and the piece index is flipped by the
+// row's line number within the 16.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  return (r / (256 / D)) & (D / 16 - 1);
+}
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
 // 16 bytes per lane from sbase + voff (global memory) into LDS at byte
 // address lds_base + 16 * lane (global_load_lds_dwordx4; sbase and lds_base
 // wave-uniform).  Issued as asm: a DMA the compiler knows of makes it wait
@@ -225,7 +236,13 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
   constexpr bool F8 = FEAT & kFp8;
-  constexpr bool Q8 = FEAT & kQ8;  // fp8 query codes (widened exactly to T)
+  constexpr bool Q8 = FEAT & kQ8;  // fp8 query codes
+  // fp8 query over an fp8 cache: S^T = K Q^T runs on the fp8 MFMA
+  // (32x32x64, e4m3 x e4m3, exact products, fp32 sums) straight from the
+  // staged fp8 K tile; only V is widened to 16 bits for the PV product
+  constexpr bool QK8 = F8 && Q8;
+  constexpr int K8S = D / 64;                // fp8 QK steps of 64 head dims
+  constexpr int NQL = QK8 ? 2 * K8S : (D / 16);  // Q load instructions
   constexpr int NW = kNW<D>;
   constexpr int NST = kNST<D>;
   constexpr int TB = kTileBytes<D>;
@@ -361,9 +378,11 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   const uint32_t row_bytes = static_cast<uint32_t>(a.Hkv) * RBC;
   const uint32_t smem0 = lds_addr(smem);
   // the piece that belongs at this lane's slot of instruction i's row (an
-  // fp8 stage is stored unpermuted: the widening pass applies the swizzle)
+  // fp8 stage is stored unpermuted, the widening pass applying the
+  // swizzle, except an fp8 K stage that the fp8 MFMA reads itself)
   auto dma_row = [&](int i) { return wave * RW + i * ROWS_PER_I + lane / (RBC / 16); };
   auto dma_kp = [&](int i) {
+    if constexpr (QK8) return ((lane % (RBC / 16)) ^ swz8<D>(dma_row(i))) * 16;
     return F8 ? (lane % (RBC / 16)) * 16 : ((lane % (RB / 16)) ^ swz_k<D>(dma_row(i))) * 16;
   };
   auto dma_vp = [&](int i) {
@@ -425,10 +444,17 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   // also counts the DMAs in flight.  They complete before the prologue's
   // final wait (loads complete in order) and are claimed after it.
   v8s qf[KQ];
-  u32x2 q8[Q8 ? KQ : 1];  // an fp8 query's codes, widened after the wait
+  u32x2 q8[Q8 && !QK8 ? KQ : 1];  // an fp8 query's codes, widened after the wait
+  v8s q8x[QK8 ? 2 * K8S : 1];     // fp8 MFMA: its codes as B operands (2 x 16 bytes per step)
   {
     const int64_t qtok = row_ok ? q0 + tok0 + tk : q0;  // rows past the tile read a valid row
-    if constexpr (Q8) {
+    if constexpr (QK8) {
+      // step s: head dims 64 s + 32 g2 + [0, 32)
+      const uint8_t* qrow =
+          reinterpret_cast<const uint8_t*>(a.q) + (qtok * a.Hq + head) * D + 32 * g2;
+#pragma unroll
+      for (int i = 0; i < 2 * K8S; ++i) q8x[i] = load16_async(qrow + 64 * (i >> 1) + 16 * (i & 1));
+    } else if constexpr (Q8) {
       const uint8_t* qrow =
           reinterpret_cast<const uint8_t*>(a.q) + (qtok * a.Hq + head) * D + 8 * g2;
 #pragma unroll
@@ -443,7 +469,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     // tile 0's block id once the ids (issued before Q) landed: the wait and
     // the read are one asm block, so nothing reads the loading register
     int blk;
-    asm volatile("s_waitcnt vmcnt(%1)\n\tv_readfirstlane_b32 %0, %2" : "=s"(blk) : "i"(KQ), "v"(ids));
+    asm volatile("s_waitcnt vmcnt(%1)\n\tv_readfirstlane_b32 %0, %2" : "=s"(blk) : "i"(NQL), "v"(ids));
     issue_tile(t_begin, blk, 0);
   }
 
@@ -473,6 +499,14 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk)
     k_lane[kk] = smem0 + r32 * RB + 16 * ((2 * kk + g2) ^ swz_k<D>(r32));
+  // ---- the fp8 MFMA's K operand: rows h2*32 + r32 of the fp8 stage, head
+  //      dims 64 s + 32 g2 + [0, 32) = 16-byte pieces 4 s + 2 g2 + t
+  uint32_t k8_lane[QK8 ? 2 * K8S : 1];
+  if constexpr (QK8) {
+#pragma unroll
+    for (int i = 0; i < 2 * K8S; ++i)
+      k8_lane[i] = smem0 + r32 * RBC + 16 * ((4 * (i >> 1) + 2 * g2 + (i & 1)) ^ swz8<D>(r32));
+  }
 
   // ---- V operand of O^T += V^T P^T: step s holds V[16s + 4*g2 + [0,4)][d] and
   //      V[16s + 8 + 4*g2 + [0,4)][d] for d = dc*32 + r32, two transpose reads.
@@ -594,6 +628,40 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
+    if constexpr (QK8) {
+      // KOFF: the fp8 stage; per step and row half, 32 bytes of K codes
+      v8s kf[4 * K8S];
+#pragma unroll
+      for (int i = 0; i < 2 * K8S; ++i)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) kf[2 * i + h2] = lds_load16(k8_lane[i] + KOFF + h2 * 32 * RBC);
+#pragma unroll
+      for (int st = 0; st < K8S; ++st)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const v8s lo = kf[2 * (2 * st) + h2], hi = kf[2 * (2 * st + 1) + h2];
+          const v8i av = __builtin_shufflevector(__builtin_bit_cast(v4i, lo), __builtin_bit_cast(v4i, hi),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+          const v8i bv = __builtin_shufflevector(__builtin_bit_cast(v4i, q8x[2 * st]),
+                                                 __builtin_bit_cast(v4i, q8x[2 * st + 1]), 0, 1, 2, 3,
+                                                 4, 5, 6, 7);
+          // e4m3 x e4m3 (format 0 for both), unit scales (E8M0 127)
+          sacc[h2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, sacc[h2], 0, 0, 0, 127,
+                                                                     0, 127);
+        }
+      // schedule: 4 reads ahead, then one MFMA per two reads
+      constexpr int NR = 4 * K8S, LEAD = 4, MID = (NR - LEAD) / 2;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < MID; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * K8S - MID, 0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     // (reads written out first: the pinned interleave below then applies)
     v8s kf[2 * KQ];
 #pragma unroll
@@ -649,6 +717,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   //      the operand swizzles, then a barrier.  Every wave widens its rows of
   //      every tile, also of tiles it skips itself.
   auto widen = [&](int stage) {
+    // (with the fp8 MFMA only V is widened)
     const char* k8 = smem + stage * 2 * TBC;
     const char* v8 = k8 + TBC;
     char* k16 = smem + NST * 2 * TBC;
@@ -661,12 +730,14 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       const int q = lane + 64 * i;
       const int r = wave * RW + q / PPR;
       const int c = q % PPR;
-      const u32x2 kw = *reinterpret_cast<const u32x2*>(k8 + r * RBC + 8 * c);
+      if constexpr (!QK8) {
+        const u32x2 kw = *reinterpret_cast<const u32x2*>(k8 + r * RBC + 8 * c);
+        const v4s k0 = T::from_fp8x4(kw[0]), k1 = T::from_fp8x4(kw[1]);
+        *reinterpret_cast<v8s*>(k16 + r * RB + 16 * (c ^ swz_k<D>(r))) =
+            v8s{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      }
       const u32x2 vw = *reinterpret_cast<const u32x2*>(v8 + r * RBC + 8 * c);
-      const v4s k0 = T::from_fp8x4(kw[0]), k1 = T::from_fp8x4(kw[1]);
       const v4s v0 = T::from_fp8x4(vw[0]), v1 = T::from_fp8x4(vw[1]);
-      *reinterpret_cast<v8s*>(k16 + r * RB + 16 * (c ^ swz_k<D>(r))) =
-          v8s{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
       *reinterpret_cast<v8s*>(v16 + r * RB + 16 * (c ^ swz_v<D>(r))) =
           v8s{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     }
@@ -677,9 +748,17 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   wait_vmcnt<0>();
   claim(ids);
   lds_barrier();
+  if constexpr (QK8) {
 #pragma unroll
-  for (int kk = 0; kk < KQ; ++kk) {
-    if constexpr (Q8) {
+    for (int i = 0; i < 2 * K8S; ++i) {
+      claim(q8x[i]);
+      const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};  // (code 0 is +0)
+      if (!row_ok) q8x[i] = z;
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < (QK8 ? 0 : KQ); ++kk) {
+    if constexpr (Q8 && !QK8) {
       claim(q8[kk]);
       const v4s lo = T::from_fp8x4(q8[kk][0]), hi = T::from_fp8x4(q8[kk][1]);
       qf[kk] = v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -723,7 +802,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
       if (!decltype(masked_c)::value || tile_active(kbase)) {
         v16f sacc[2];
         v8s pb[4];
-        qk(koff, sacc);
+        qk(QK8 ? stage * 2 * TBC : koff, sacc);
         softmax(sacc, kbase, pb, masked_c);
         pv(koff, pb);
       }

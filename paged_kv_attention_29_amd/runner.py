@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import (merge_attn_states, paged_attn_decode, paged_attn_decode_merged, paged_attn_prefill,
-               reshape_and_cache)
+               reshape_and_cache, scaled_fp8_quant)
 
 
 @dataclass
@@ -60,6 +60,9 @@ class PagedCache:
         self.block_table = torch.from_numpy(w.block_table).to(device)
         self.alibi = None if w.alibi_slopes is None else w.alibi_slopes.to(device)
         self.sinks = None  # optional fp32 [num_heads] attention-sink logits on the device
+        # fp8 cache only: a device fp32 scalar; the calls then quantise q with
+        # it (scaled_fp8_quant) and attend the codes with this descale
+        self.q_scale = None
 
     def write(self, key: torch.Tensor, value: torch.Tensor, slots: torch.Tensor) -> None:
         reshape_and_cache(key.to(self.device), value.to(self.device), self.key_cache,
@@ -91,8 +94,12 @@ class PagedCache:
         if call.kind == "decode" and S > 1 and merged:
             cnt = torch.zeros(T * w.num_heads, dtype=torch.int32, device=dev)
         ids = torch.from_numpy(np.asarray(call.seq_ids, dtype=np.int64)).to(dev)
+        q = call.q.to(dev)
+        if self.q_scale is not None:
+            q = scaled_fp8_quant(torch.empty(q.shape, dtype=torch.uint8, device=dev), q,
+                                 self.q_scale)
         return CallBuffers(
-            kind=call.kind, q=call.q.to(dev),
+            kind=call.kind, q=q,
             cu_seqlens_q=torch.from_numpy(call.cu_seqlens_q).to(dev),
             seq_lens=torch.from_numpy(call.seq_lens.astype(np.int32)).to(dev),
             block_table=self.block_table.index_select(0, ids).contiguous(),
@@ -107,24 +114,26 @@ class PagedCache:
                                cb.seq_lens, cb.block_table, cb.max_seqlen_q, cb.max_seqlen_k,
                                w.scale, cb.causal, w.window_left, w.softcap, self.alibi, lse=cb.lse,
                                stream=stream, sinks=self.sinks, k_scale=self.k_scale,
-                               v_scale=self.v_scale)
+                               v_scale=self.v_scale, q_scale=self.q_scale)
         elif cb.num_splits == 1:
             paged_attn_decode(cb.out, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
                               self.alibi, 1, lse=cb.lse, stream=stream, sinks=self.sinks,
-                              k_scale=self.k_scale, v_scale=self.v_scale)
+                              k_scale=self.k_scale, v_scale=self.v_scale, q_scale=self.q_scale)
         elif cb.split_counters is not None:
             paged_attn_decode_merged(cb.out, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                                      cb.block_table, cb.max_seqlen_k, w.scale, cb.num_splits,
                                      cb.part_out, cb.part_lse, cb.split_counters, w.window_left,
                                      w.softcap, self.alibi, lse=cb.lse, stream=stream,
-                                     sinks=self.sinks, k_scale=self.k_scale, v_scale=self.v_scale)
+                                     sinks=self.sinks, k_scale=self.k_scale, v_scale=self.v_scale,
+                                     q_scale=self.q_scale)
         else:
             paged_attn_decode(None, cb.q, self.key_cache, self.value_cache, cb.seq_lens,
                               cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
                               self.alibi, cb.num_splits, part_out=cb.part_out,
                               part_lse=cb.part_lse, stream=stream, sinks=self.sinks,
-                              k_scale=self.k_scale, v_scale=self.v_scale)
+                              k_scale=self.k_scale, v_scale=self.v_scale, q_scale=self.q_scale,
+                              out_dtype=w.dtype)
             merge_attn_states(cb.out, cb.part_out, cb.part_lse, out_lse=cb.lse, stream=stream)
 
 
