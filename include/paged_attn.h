@@ -458,6 +458,21 @@ int pa_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
                      const int32_t* seq_lens, int num_seqs, int64_t num_blocks,
                      int block_size, int32_t* counts, void* stream);
 
+/*
+ * pa_trace_set — timeline tracing, for profiling (not part of the
+ * attention path).  Only the trace build of the library
+ * (libpagedattn_trace.so, built with PA_TRACE=1) records anything; the
+ * regular library returns PA_ERR_UNSUPPORTED.  buffer: NULL (off), or a
+ * device array of 16 uint64 per workgroup of the largest prefill / decode
+ * launch that follows; each workgroup writes shader-clock times of its
+ * phases (entry, work item known, key loop start, key loop end, results
+ * stored), its CU's HW_ID and XCC_ID, the key tiles or steps it ran, its
+ * item (sequence << 32 | query tile or split) and each wave's end time.
+ * The times of different shader engines are not on one clock.  Process-
+ * wide setting; launches that overlap share the buffer.
+ */
+int pa_trace_set(void* buffer);
+
 /* Message describing the last non-OK return on the calling thread ("" if
  * none).  The string is owned by the library and valid until the next call
  * on this thread. */

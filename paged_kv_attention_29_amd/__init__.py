@@ -41,7 +41,10 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libpagedattn.so")
+# PA_TRACE=1 loads the trace build (timeline trace points compiled in; see
+# pa_trace_set and trace_timeline.py)
+library_path = os.path.join(
+    _HERE, "libpagedattn_trace.so" if os.environ.get("PA_TRACE") == "1" else "libpagedattn.so")
 
 PA_F16, PA_BF16, PA_F32, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
@@ -86,10 +89,13 @@ def _load() -> ctypes.CDLL:
     lib.pa_local_virtual_batches.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
                                              _vp, _vp, _vp]
     for fn in ("reshape_and_cache", "paged_attn_prefill", "paged_attn_decode",
-               "paged_attn_decode_noalloc", "merge_attn_states", "scaled_fp8_quant",
+               "paged_attn_decode_noalloc", "paged_attn_decode_merged", "merge_attn_states",
+               "scaled_fp8_quant",
                "pa_use_cascade",
                "pa_check_indices", "paged_attn_cascade", "pa_local_virtual_batches"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.pa_trace_set.argtypes = [_vp]
+    lib.pa_trace_set.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     return lib

@@ -11,6 +11,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
+# the trace library: the same sources with the timeline trace points compiled
+# in (pa_trace_set; PA_TRACE=1 makes the package load it)
+TRACE_LIB = os.path.join(HERE, "libpagedattn_trace.so")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "reshape_and_cache.hip", "merge.hip", "decode.hip", "prefill.hip",
            "check.hip", "cascade.hip", "local.hip", "probe.hip", "noalloc.hip"]
@@ -40,25 +43,28 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, trace: bool = False) -> str:
+    out_dir = BUILD + ("_trace" if trace else "")
+    lib_path = TRACE_LIB if trace else LIB
+    os.makedirs(out_dir, exist_ok=True)
     hipcc = _hipcc()
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *EXTRA.get(src, []), *(["-DPA_TRACE=1"] if trace else []),
+                     "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
         for r in ex.map(_run, cmds):
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout + r.stderr, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))

@@ -11,7 +11,10 @@
 #include <cstdio>
 #include <string>
 
+#include <atomic>
+
 #include "../../include/paged_attn.h"
+#include "common.h"
 #include "launch.h"
 
 namespace {
@@ -184,9 +187,23 @@ pa::AttnParams decode_params(void* out, float* lse, float* part_out, float* part
 
 }  // namespace
 
+// the trace buffer the launchers hand to the kernels (see pa_trace_set)
+namespace pa {
+std::atomic<uint64_t*> g_trace_buf{nullptr};
+uint64_t* trace_buffer() { return g_trace_buf.load(); }
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_trace_set(void* buffer) {
+  if (!pa::kTrace)
+    return fail(PA_ERR_UNSUPPORTED, "pa_trace_set: this library is built without tracing "
+                                    "(build.py --trace builds libpagedattn_trace.so)");
+  pa::g_trace_buf.store(static_cast<uint64_t*>(buffer));
+  return ok();
+}
 
 int reshape_and_cache(const void* key, const void* value, int64_t key_token_stride,
                       int64_t value_token_stride, void* key_cache, void* value_cache,

@@ -112,6 +112,46 @@ struct F16 {
 };
 
 // ---------------------------------------------------------------------------
+// Timeline tracing.  Built with -DPA_TRACE=1 (the separate trace library),
+// the prefill and decode kernels record per workgroup kTraceSlots 64-bit
+// words at trace + workgroup * kTraceSlots: shader-clock times of their
+// phases, the CU's HW_ID and XCC_ID and the work done.  Otherwise the
+// trace points compile to nothing.  The clock (s_memtime) is not shared by
+// all shader engines: compare times within one CU only.
+// ---------------------------------------------------------------------------
+#ifndef PA_TRACE
+#define PA_TRACE 0
+#endif
+constexpr bool kTrace = PA_TRACE != 0;
+constexpr int kTraceSlots = 16;
+enum TraceSlot {
+  kTrEntry = 0,    // kernel entry
+  kTrItem = 1,     // work item known (after the lookup / ranking)
+  kTrLoop0 = 2,    // first K/V data landed: the key loop starts
+  kTrLoop1 = 3,    // key loop done
+  kTrEnd = 4,      // results stored (wave 0)
+  kTrHwId = 5,     // HW_ID register (CU, SH, SE)
+  kTrXcc = 6,      // XCC_ID register
+  kTrUnits = 7,    // key tiles (prefill) or key steps (decode) of the item
+  kTrWho = 8,      // item: sequence << 32 | query tile (prefill) or split (decode)
+  kTrWaveEnd = 9,  // .. 12: each wave's end time
+};
+__device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memtime(); }
+// lane 0 of the calling wave stores v into slot k of this workgroup's record
+__device__ __forceinline__ void trace_put(uint64_t* trace, int k, uint64_t v) {
+  if constexpr (kTrace) {
+    if (trace != nullptr && (threadIdx.x & 63) == 0)
+      __builtin_nontemporal_store(v, trace + (uint64_t)blockIdx.x * kTraceSlots + k);
+  }
+}
+__device__ __forceinline__ void trace_hw(uint64_t* trace) {
+  if constexpr (kTrace) {
+    trace_put(trace, kTrHwId, __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11)));
+    trace_put(trace, kTrXcc, __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // wave64 cross-lane helpers
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) {

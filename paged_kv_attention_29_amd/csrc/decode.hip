@@ -73,6 +73,8 @@ struct DecodeArgs {
   // group) to finish merges the partial results into out / lse.  Null: the
   // partials are the result.
   int* counters;
+  // timeline trace records (trace library only), or null
+  uint64_t* trace;
 };
 
 enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4, kQ8 = 8 };
@@ -769,6 +771,7 @@ template <typename T, int D, int FEAT, int HPW>
 __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(DecodeArgs a) {
   using K = Dec<T, D, FEAT, HPW>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  const uint64_t t_entry = kTrace ? trace_clock() : 0;
   if constexpr (K::F8) {
     // the K scale multiplies every score
     const float ks = *a.k_scale;
@@ -810,11 +813,24 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
 
   const typename K::Item it = K::make_item(a, grp, b, split, L);
   int* const flag = reinterpret_cast<int*>(smem + rank_slot_offset<D, HPW, K::F8>(a.G));
+  if constexpr (kTrace) {
+    if (wave == 0) {
+      trace_put(a.trace, kTrEntry, t_entry);
+      trace_put(a.trace, kTrItem, trace_clock());
+      trace_put(a.trace, kTrUnits,
+                static_cast<uint64_t>(it.lo_vis < it.hi ? max(it.s_end - it.s_begin, 0) : 0));
+      trace_put(a.trace, kTrWho, (uint64_t)b << 32 | static_cast<uint32_t>(split));
+      trace_hw(a.trace);
+    }
+  }
   if (it.lo_vis >= it.hi) {
     // (merged: only split 0 of a group holding the sinks writes a partial)
     const bool write = a.counters == nullptr || (split == 0 && a.sinks != nullptr);
     if (write) K::emit_empty(a, it);
     if (a.counters != nullptr) merged_tail<K>(a, it, grp, L, write, flag);
+    if constexpr (kTrace) {
+      if (wave == 0) trace_put(a.trace, kTrEnd, trace_clock());
+    }
     return;
   }
   const bool col_ok = r16 < it.nc;
@@ -844,6 +860,9 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
     K::fetch_ids(a, it, min(step + kWaves, it.s_end - 1), ids);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first step landed
+  if constexpr (kTrace) {
+    if (wave == 0) trace_put(a.trace, kTrLoop0, trace_clock());
+  }
   v8s qf[HPW][K::KK];
   K::mask_q(qraw, col_ok, hsel, qf);
   for (; step < it.s_end; step += kWaves) {
@@ -857,8 +876,16 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
     K::compute_step(a, it, step, cur, qf, slope_log2, r16, c4, hsel, vs, m_run, l_run, o);
     cur = nxt;
   }
+  if constexpr (kTrace) {
+    if (wave == 0) trace_put(a.trace, kTrLoop1, trace_clock());
+  }
   K::combine_emit(a, it, wave, r16, c4, m_run, l_run, o, reinterpret_cast<float*>(smem));
   if (a.counters != nullptr) merged_tail<K>(a, it, grp, L, true, flag);
+  if constexpr (kTrace) {
+    const uint64_t t_end = trace_clock();
+    if (wave == 0) trace_put(a.trace, kTrEnd, t_end);
+    trace_put(a.trace, kTrWaveEnd + wave, t_end);
+  }
 }
 
 template <typename T, int D, int FEAT, int HPW>
@@ -950,6 +977,7 @@ int launch_decode(const AttnParams& p, hipStream_t stream) {
   a.v_scale = p.v_scale;
   a.q_scale = p.q_scale;
   a.counters = p.num_splits > 1 ? p.split_counters : nullptr;
+  a.trace = trace_buffer();
   const bool alibi = p.alibi_slopes != nullptr;
   if (p.kv_fp8 && p.q_scale != nullptr) {
     if (p.dtype == kBF16) return launch_t<BF16, kFp8 | kQ8>(a, p.head_size, softcap, alibi, stream);

@@ -77,6 +77,10 @@ constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
 // (looked up once per device).  Returns 0, or -3 when HIP reports an error.
 int noalloc_scratch(void** ptr);
 
+// The timeline trace buffer the kernels write (trace library only; null:
+// no tracing).  Set by pa_trace_set, read by the launchers.
+uint64_t* trace_buffer();
+
 // host-side rewriting for chunked local attention; returns the number of
 // virtual sequences (outputs NULL: count only)
 int local_virtual_batches(int chunk, int block_size, const int32_t* qsl, const int32_t* seq_lens,

@@ -85,6 +85,8 @@ struct PrefillArgs {
   // fp8 query (with an fp8 cache): q holds e4m3 codes and this device fp32
   // scalar is their descale; null for a 16-bit query
   const float* q_scale;
+  // timeline trace records (trace library only), or null
+  uint64_t* trace;
 };
 
 // Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   static_assert(NI >= 1 && RW <= 16, "tile split");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
+  const uint64_t t_entry = kTrace ? trace_clock() : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -308,7 +311,10 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     const int cl = fin ? a.seq_lens[c] : 0;
     const int cb = fin && wave_blk < a.bt_stride ? a.block_table[(int64_t)c * a.bt_stride + wave_blk] : 0;
     const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in && cq / tok + c <= t));
-    if (k == 0) return;  // below S_0 (cu_q[0] > 0)
+    if (k == 0) {  // below S_0 (cu_q[0] > 0)
+      if (wave == 0) trace_put(a.trace, kTrEntry, t_entry);
+      return;
+    }
     lo += (k - 1) * step;
     if (step == 1) {
       q0 = __builtin_amdgcn_readlane(cq, k - 1);
@@ -322,9 +328,21 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   const int b = lo;
   const int nq = q1 - q0;
   const int local = t - (q0 / tok + b);
-  if (local >= (nq + tok - 1) / tok) return;  // an empty slot
+  if (local >= (nq + tok - 1) / tok) {  // an empty slot
+    if constexpr (kTrace) {
+      if (wave == 0) {
+        trace_put(a.trace, kTrEntry, t_entry);
+        trace_put(a.trace, kTrEnd, trace_clock());
+        trace_hw(a.trace);
+      }
+    }
+    return;
+  }
   const int qt = (nq + tok - 1) / tok - 1 - local;
   const int tok0 = qt * tok;
+  if constexpr (kTrace) {
+    if (wave == 0) trace_put(a.trace, kTrItem, trace_clock());
+  }
   const int ctx = L - nq;
   const int ntok = min(nq - tok0, a.tok_per_tile);
   const int p_first = ctx + tok0;
@@ -748,6 +766,15 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   wait_vmcnt<0>();
   claim(ids);
   lds_barrier();
+  if constexpr (kTrace) {
+    if (wave == 0) {
+      trace_put(a.trace, kTrEntry, t_entry);
+      trace_put(a.trace, kTrLoop0, trace_clock());
+      trace_put(a.trace, kTrUnits, static_cast<uint64_t>(n));
+      trace_put(a.trace, kTrWho, (uint64_t)b << 32 | static_cast<uint32_t>(qt));
+      trace_hw(a.trace);
+    }
+  }
   if constexpr (QK8) {
 #pragma unroll
     for (int i = 0; i < 2 * K8S; ++i) {
@@ -835,6 +862,9 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     for (int j = 0; j < n; ++j) step(j, j & 1, std::false_type{}, std::false_type{});
   }
 
+  if constexpr (kTrace) {
+    if (wave == 0) trace_put(a.trace, kTrLoop1, trace_clock());
+  }
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
   float l_tot = l_run + shfl_xor(l_run, 32);
   float m_fin = m_run, o_scale = 1.0f;
@@ -886,6 +916,11 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     const int64_t qrow = q0 + tok0 + tk;
     a.lse[(part * a.Hq + head) * a.total_q + qrow] =
         l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+  if constexpr (kTrace) {
+    const uint64_t t_end = trace_clock();
+    if (wave == 0) trace_put(a.trace, kTrEnd, t_end);
+    trace_put(a.trace, kTrWaveEnd + wave, t_end);
   }
 }
 
@@ -968,6 +1003,7 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.k_scale = p.k_scale;
   a.v_scale = p.v_scale;
   a.q_scale = p.q_scale;
+  a.trace = trace_buffer();
   const int ns = p.key_split > 0 ? (p.max_seqlen_k + p.key_split - 1) / p.key_split : 1;
   const bool alibi = p.alibi_slopes != nullptr;
   if (p.kv_fp8 && p.q_scale != nullptr) {
