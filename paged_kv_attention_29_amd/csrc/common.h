@@ -135,8 +135,11 @@ enum TraceSlot {
   kTrUnits = 7,    // key tiles (prefill) or key steps (decode) of the item
   kTrWho = 8,      // item: sequence << 32 | query tile (prefill) or split (decode)
   kTrWaveEnd = 9,  // .. 12: each wave's end time
+  kTrRealEntry = 13,  // constant-rate (100 MHz) clock at entry
+  kTrRealEnd = 14,    // and when wave 0 stored its results
 };
 __device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memtime(); }
+__device__ __forceinline__ uint64_t trace_realclock() { return __builtin_amdgcn_s_memrealtime(); }
 // lane 0 of the calling wave stores v into slot k of this workgroup's record
 __device__ __forceinline__ void trace_put(uint64_t* trace, int k, uint64_t v) {
   if constexpr (kTrace) {

@@ -772,6 +772,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   using K = Dec<T, D, FEAT, HPW>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t t_entry = kTrace ? trace_clock() : 0;
+  const uint64_t r_entry = kTrace ? trace_realclock() : 0;
   if constexpr (K::F8) {
     // the K scale multiplies every score
     const float ks = *a.k_scale;
@@ -816,6 +817,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   if constexpr (kTrace) {
     if (wave == 0) {
       trace_put(a.trace, kTrEntry, t_entry);
+      trace_put(a.trace, kTrRealEntry, r_entry);
       trace_put(a.trace, kTrItem, trace_clock());
       trace_put(a.trace, kTrUnits,
                 static_cast<uint64_t>(it.lo_vis < it.hi ? max(it.s_end - it.s_begin, 0) : 0));
@@ -883,7 +885,10 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks<D>) void decode_kernel(Deco
   if (a.counters != nullptr) merged_tail<K>(a, it, grp, L, true, flag);
   if constexpr (kTrace) {
     const uint64_t t_end = trace_clock();
-    if (wave == 0) trace_put(a.trace, kTrEnd, t_end);
+    if (wave == 0) {
+      trace_put(a.trace, kTrEnd, t_end);
+      trace_put(a.trace, kTrRealEnd, trace_realclock());
+    }
     trace_put(a.trace, kTrWaveEnd + wave, t_end);
   }
 }

@@ -260,6 +260,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const uint64_t t_entry = kTrace ? trace_clock() : 0;
+  const uint64_t r_entry = kTrace ? trace_realclock() : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -769,6 +770,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   if constexpr (kTrace) {
     if (wave == 0) {
       trace_put(a.trace, kTrEntry, t_entry);
+      trace_put(a.trace, kTrRealEntry, r_entry);
       trace_put(a.trace, kTrLoop0, trace_clock());
       trace_put(a.trace, kTrUnits, static_cast<uint64_t>(n));
       trace_put(a.trace, kTrWho, (uint64_t)b << 32 | static_cast<uint32_t>(qt));
@@ -919,7 +921,10 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   }
   if constexpr (kTrace) {
     const uint64_t t_end = trace_clock();
-    if (wave == 0) trace_put(a.trace, kTrEnd, t_end);
+    if (wave == 0) {
+      trace_put(a.trace, kTrEnd, t_end);
+      trace_put(a.trace, kTrRealEnd, trace_realclock());
+    }
     trace_put(a.trace, kTrWaveEnd + wave, t_end);
   }
 }

@@ -35,6 +35,7 @@ from paged_kv_attention_29_amd import runner  # noqa: E402
 
 SLOTS = 16
 ENTRY, ITEM, LOOP0, LOOP1, END, HWID, XCC, UNITS, WHO, WAVE_END = range(10)
+REAL_ENTRY, REAL_END = 13, 14  # 100 MHz clock
 
 
 def run(workload: str, splits: int, max_wgs: int):
@@ -65,23 +66,29 @@ def run(workload: str, splits: int, max_wgs: int):
     rc = pa.lib.pa_trace_set(buf.data_ptr())
     if rc != 0:
         raise RuntimeError(pa.lib.pa_last_error().decode())
-    float(flush.sum())
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    if workload == "decode" and cb.num_splits > 1:
-        # the decode launch alone (no merge), the trace's subject
-        pa.paged_attn_decode(None, cb.q, cache.key_cache, cache.value_cache, cb.seq_lens,
-                             cb.block_table, cb.max_seqlen_k, w.scale, w.window_left, w.softcap,
-                             cache.alibi, cb.num_splits, part_out=cb.part_out,
-                             part_lse=cb.part_lse)
-    else:
-        cache.run(cb)
-    e1.record()
-    torch.cuda.synchronize()
+
+    def launch():
+        float(flush.sum())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if workload == "decode" and cb.num_splits > 1:
+            # the decode launch alone (no merge), the trace's subject
+            pa.paged_attn_decode(None, cb.q, cache.key_cache, cache.value_cache, cb.seq_lens,
+                                 cb.block_table, cb.max_seqlen_k, w.scale, w.window_left,
+                                 w.softcap, cache.alibi, cb.num_splits, part_out=cb.part_out,
+                                 part_lse=cb.part_lse)
+        else:
+            cache.run(cb)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms = launch()
     pa.lib.pa_trace_set(None)
+    ms_plain = launch()  # the same launch with the trace off, for comparison
     t = buf.view(max_wgs, SLOTS).cpu().numpy().astype(np.int64)
-    return w, e0.elapsed_time(e1), t[t[:, ENTRY] != 0]
+    return w, (ms, ms_plain), t[t[:, ENTRY] != 0]
 
 
 def cu_key(rec):
@@ -98,7 +105,8 @@ def summarise(workload, w, ms, t):
     end = np.where(real, np.maximum(t[:, END], wave_end), t[:, END])
     med = lambda x: int(np.median(x)) if len(x) else 0
     lines = [f"## {workload}: {w.name}", "",
-             f"launch {ms * 1e3:.1f} us (HIP events, after a 512 MiB read); "
+             f"launch {ms[0] * 1e3:.1f} us traced, {ms[1] * 1e3:.1f} us with the trace off "
+             f"(HIP events, after a 512 MiB read); "
              f"{len(t)} workgroups with a record, {int(real.sum())} with work", "",
              "| phase (shader-clock cycles, per workgroup) | median | mean |",
              "|---|---|---|"]
@@ -110,6 +118,19 @@ def summarise(workload, w, ms, t):
     for name, x in phases:
         lines.append(f"| {name} | {med(x)} | {int(np.mean(x))} |")
     lines.append(f"| tiles or steps per workgroup | {med(r[:, UNITS])} | {np.mean(r[:, UNITS]):.1f} |")
+    # the shader clock's rate: its ticks over the constant 100 MHz clock's,
+    # per workgroup, from entry to wave 0's end
+    dr = r[:, REAL_END] - r[:, REAL_ENTRY]
+    ok = dr > 0
+    ghz = (r[ok, END] - r[ok, ENTRY]) / dr[ok] * 0.1
+    if ok.any():
+        span = (r[ok, REAL_END].max() - r[ok, REAL_ENTRY].min()) / 100.0
+        lines += ["", f"first workgroup entry -> last workgroup end (100 MHz clock, "
+                  f"workgroups with work): {span:.1f} us"]
+    if len(ghz):
+        lines += ["", f"shader clock over the launch (s_memtime ticks per 10 ns of s_memrealtime, "
+                  f"per workgroup): median {np.median(ghz):.2f} GHz, "
+                  f"10th-90th percentile {np.percentile(ghz, 10):.2f}-{np.percentile(ghz, 90):.2f} GHz"]
     # per CU: occupancy, ramp, tail
     occ = np.zeros(4)
     tot = 0
