@@ -10,8 +10,9 @@ Inputs are seeded synthetic data resident in HBM before timing starts.  Each
 step uses the next of `--layers` independent caches (as consecutive layers of
 a model would) so no step re-reads K/V another step left in the caches.
 
-`--kv-fp8` runs the decode workloads over an fp8 (e4m3) cache with
-per-tensor scales (the bytes then count one byte per element).
+`--kv-fp8` runs the workloads over an fp8 (e4m3) cache with per-tensor
+scales and an fp8 query (`--fp8-q16` keeps the 16-bit query); the bytes then
+count one byte per element.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on a
 single GPU.
