@@ -14,8 +14,8 @@ gfx950 assembly of every prefill instantiation:
    stores or atomics, its write-back or discard): stores and atomics
    (including the decode work counter) are vector-memory instructions.
 
-CPU only: it compiles the kernel source with hipcc and the library build's
-flags (skipped if hipcc is missing)."""
+CPU only: it compiles the kernel sources with hipcc and the library build's
+flags, all at once (skipped if hipcc is missing)."""
 import importlib.util
 import os
 import re
@@ -38,16 +38,33 @@ def _build_flags(src):
     return [*mod.FLAGS, *mod.EXTRA.get(src, [])]
 
 
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
 @pytest.fixture(scope="module")
-def prefill_asm(tmp_path_factory):
+def all_asm(tmp_path_factory):
+    """gfx950 assembly of every kernel source, compiled concurrently (one
+    hipcc per source) with the library build's flags."""
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "prefill.s"
-    cmd = [hipcc, *_build_flags("prefill.hip"), "--cuda-device-only", "-S",
-           os.path.join(CSRC, "prefill.hip"), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True)
-    text = out.read_text()
+    d = tmp_path_factory.mktemp("isa")
+    procs = {}
+    for src in SOURCES:
+        cmd = [hipcc, *_build_flags(src), "--cuda-device-only", "-S",
+               os.path.join(CSRC, src), "-o", str(d / (src + ".s"))]
+        procs[src] = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE)
+    texts = {}
+    for src, proc in procs.items():
+        _, err = proc.communicate()
+        assert proc.returncode == 0, f"{src}: {err.decode()[-2000:]}"
+        texts[src] = (d / (src + ".s")).read_text()
+    return texts
+
+
+@pytest.fixture(scope="module")
+def prefill_asm(all_asm):
+    text = all_asm["prefill.hip"]
     funcs = {}
     for name in re.findall(r"^(_Z\S*prefill_kernel\S*):", text, flags=re.M):
         start = text.index(name + ":")
@@ -117,15 +134,9 @@ def test_lds_dma_waits_after_m0_write(prefill_asm):
     assert n_dma > 0
 
 
-@pytest.mark.parametrize("src", sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")))
-def test_no_scalar_cache_writes(src, tmp_path):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available")
-    out = tmp_path / (src + ".s")
-    subprocess.run([hipcc, *_build_flags(src), "--cuda-device-only", "-S",
-                    os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
-    bad = [l.strip() for l in out.read_text().split("\n")
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_scalar_cache_writes(src, all_asm):
+    bad = [l.strip() for l in all_asm[src].split("\n")
            if re.match(r"\s*(s_atomic|s_store|s_buffer_store|s_scratch_store|s_dcache_wb|"
                        r"s_dcache_discard)", l)]
     assert not bad, f"{src}: {bad[:3]}"
