@@ -14,8 +14,8 @@ a model would) so no step re-reads K/V another step left in the caches.
 scales and an fp8 query (`--fp8-q16` keeps the 16-bit query); the bytes then
 count one byte per element.
 
-Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on a
-single GPU.
+Prints ONE JSON line.  `--gpus N` with N > 1 is refused: the hot path here
+runs on a single GPU (no collectives).
 """
 from __future__ import annotations
 
