@@ -293,6 +293,27 @@ def test_prefill_edges(pa, runner, case):
     assert_lse_close(cb.lse, ref[1], name)
 
 
+@pytest.mark.timeout(300)
+def test_prefill_many_sequences(pa, runner):
+    """5 000 sequences, a fifth of them without new tokens: the prefill
+    kernel's sequence lookup takes three rounds of its 64-way search here
+    (one up to 64 sequences), and the compact tile grid holds one empty slot
+    per sequence at most."""
+    rng = np.random.default_rng(77)
+    B = 5000
+    ctx = rng.integers(0, 65, size=B)
+    q = rng.integers(1, 41, size=B) * (rng.random(B) >= 0.2)
+    _announce(f"prefill of {B} sequences, {int((q == 0).sum())} without queries")
+    w = W.custom("many_seqs", 16, ctx.tolist(), q.tolist(), 4, 2, 64, 16, torch.bfloat16,
+                 "prefill")
+    cache, res = runner.run_workload(w)
+    kc, vc = oracle_cache(w, 0)
+    ref = oracle_call(w, kc, vc, w.steps[0].calls[0])
+    cb = res[0][0]
+    assert_attn_close(cb.out, ref[0], "many sequences")
+    assert_lse_close(cb.lse, ref[1], "many sequences lse")
+
+
 @pytest.mark.parametrize("D,Hq,Hkv,ctx,q", [(128, 8, 2, [64, 0, 300], [100, 29, 70]),
                                              (64, 6, 2, [17], [150])])
 def test_prefill_noncausal_alibi(pa, runner, D, Hq, Hkv, ctx, q):
