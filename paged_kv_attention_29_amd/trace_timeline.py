@@ -5,7 +5,7 @@ build of the library (python paged_kv_attention_29_amd/build.py --trace).
     python paged_kv_attention_29_amd/trace_timeline.py --workload prefill
 
 (run as a script: PA_TRACE=1 must be set before the package loads its
-library, which `python -m` would do first)
+library, which `python -m` would do first; run() sets it)
 
 Runs the workload's call a few times, then once with pa_trace_set on (after
 reading a 512 MiB buffer, so the caches start cold as in bench.py), and
@@ -21,17 +21,12 @@ import argparse
 import os
 import sys
 
-os.environ["PA_TRACE"] = "1"  # before the package loads its library
-
 import numpy as np
-import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import workloads as W  # noqa: E402
-import paged_kv_attention_29_amd as pa  # noqa: E402
-from paged_kv_attention_29_amd import runner  # noqa: E402
 
 SLOTS = 16
 ENTRY, ITEM, LOOP0, LOOP1, END, HWID, XCC, UNITS, WHO, WAVE_END = range(10)
@@ -39,6 +34,10 @@ REAL_ENTRY, REAL_END = 13, 14  # 100 MHz clock
 
 
 def run(workload: str, splits: int, max_wgs: int):
+    os.environ["PA_TRACE"] = "1"  # before the package loads its library
+    import torch
+    import paged_kv_attention_29_amd as pa
+    from paged_kv_attention_29_amd import runner
     if workload == "decode":
         w = W.decode_batch(num_splits=splits)
         call = w.steps[0].calls[0]
