@@ -54,8 +54,13 @@ CASES = [
      torch.bfloat16, 0.0),
     ("g2_d64_fp16_cap", 64, [17, 1, 90], [3, 0, 50], 4, 2, 64, 32, torch.float16, 5.0),
     ("g1_d256", 32, [40, 9], [10, 100], 2, 2, 256, 16, torch.bfloat16, 0.0),
-    # a decode batch: one query per sequence, so the prefix pass splits its keys
+    # decode batches: one query per sequence, so the prefix pass splits its
+    # keys and the suffix pass is the split decode
     ("decode_q1_splits", 1024, [1] * 40, list(range(3, 43 * 7, 7)), 32, 8, 128, 16,
+     torch.bfloat16, 0.0),
+    ("decode_q1_g8_d256_cap", 512, [1] * 9, [0, 1, 15, 16, 17, 300, 511, 900, 64], 16, 2, 256,
+     32, torch.float16, 30.0),
+    ("decode_q1_g1_d64", 128, [1] * 70, list(range(0, 70 * 13, 13)), 4, 4, 64, 16,
      torch.bfloat16, 0.0),
 ]
 
@@ -78,6 +83,11 @@ def test_cascade_matches_oracle_and_prefill(pa, case):
     out3 = torch.empty_like(out)
     pa.paged_attn_cascade(out3, qd, kcd, vcd, cud, lensd, td, max(q_lens), max(lens), scale,
                           prefix, softcap=cap, max_prefix_splits=3)
+    # (one part for the prefix and one for the suffix)
+    out1 = torch.empty_like(out)
+    lse1 = torch.empty_like(lse)
+    pa.paged_attn_cascade(out1, qd, kcd, vcd, cud, lensd, td, max(q_lens), max(lens), scale,
+                          prefix, softcap=cap, lse=lse1, max_prefix_splits=1)
     out_p = torch.empty_like(out)
     lse_p = torch.empty_like(lse)
     pa.paged_attn_prefill(out_p, qd, kcd, vcd, cud, lensd, td, max(q_lens), max(lens), scale,
@@ -91,3 +101,5 @@ def test_cascade_matches_oracle_and_prefill(pa, case):
     assert_attn_close(out_p, ro, f"{name} plain prefill")
     assert_attn_close(out, out_p.double().cpu(), f"{name} cascade vs prefill")
     assert_attn_close(out3, ro, f"{name} cascade, at most 3 prefix splits")
+    assert_attn_close(out1, ro, f"{name} cascade, one prefix part")
+    assert_lse_close(lse1, rl, f"{name} cascade lse, one prefix part")

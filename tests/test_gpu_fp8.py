@@ -225,13 +225,17 @@ def test_prefill_fp8_cache(pa, case):
     assert_lse_close(lse, rl, f"{name} lse")
 
 
-def test_cascade_fp8_cache(pa):
-    """paged_attn_cascade over an fp8 cache (decode-like batch and longer
-    chunks) against the oracle's cascade on the dequantised cache, and the
-    fp8 plain causal prefill of the same batch."""
+@pytest.mark.parametrize("q_lens,extra", [([1, 37, 64, 1, 129], [0, 100, 7, 300, 64]),
+                                          ([1] * 12, list(range(5, 12 * 60, 60)))],
+                         ids=["chunks", "one_query_each"])
+def test_cascade_fp8_cache(pa, q_lens, extra):
+    """paged_attn_cascade over an fp8 cache (chunks of several queries, and a
+    decode batch, whose suffix pass is the split decode) against the
+    oracle's cascade on the dequantised cache, and the fp8 plain causal
+    prefill of the same batch."""
     from test_gpu_cascade import _case
-    print("\n[gpu-case] cascade fp8", flush=True)
-    prefix, q_lens, extra = 256, [1, 37, 64, 1, 129], [0, 100, 7, 300, 64]
+    print(f"\n[gpu-case] cascade fp8, q_lens {q_lens[:4]}..", flush=True)
+    prefix = 256
     Hq, Hkv, D, bs = 32, 8, 128, 16
     q, kc, vc, cu, lens, table = _case(41, prefix, q_lens, extra, Hq, Hkv, D, bs, torch.bfloat16)
     k_scale, v_scale = 0.011, 0.0075

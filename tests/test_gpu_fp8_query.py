@@ -134,11 +134,14 @@ def test_prefill_fp8_query(pa, case):
     assert_lse_close(lse, rl, f"{name} lse")
 
 
-def test_cascade_fp8_query(pa):
+@pytest.mark.parametrize("q_lens,extra", [([1, 37, 64, 1, 129], [0, 100, 7, 300, 64]),
+                                          ([1] * 12, list(range(5, 12 * 60, 60)))],
+                         ids=["chunks", "one_query_each"])
+def test_cascade_fp8_query(pa, q_lens, extra):
     from oracle.fp8 import e4m3_quantize
     from test_gpu_cascade import _case
-    print("\n[gpu-case] cascade fp8 query", flush=True)
-    prefix, q_lens, extra = 256, [1, 37, 64, 1, 129], [0, 100, 7, 300, 64]
+    print(f"\n[gpu-case] cascade fp8 query, q_lens {q_lens[:4]}..", flush=True)
+    prefix = 256
     Hq, Hkv, D, bs = 32, 8, 128, 16
     q, kc, vc, cu, lens, table = _case(43, prefix, q_lens, extra, Hq, Hkv, D, bs, torch.bfloat16)
     q = (q.float() * 0.5).to(torch.bfloat16)
