@@ -9,7 +9,9 @@
 // FlashInferMetadataBuilder, fixed_split_size), so every non-empty work
 // item of a batch is about the same size.  The G = Hq / Hkv query heads
 // sharing KV head g are the 16 columns of one MFMA tile (padded with zero
-// queries), so each K/V byte is read from HBM once for all G heads.  Keys
+// queries; with G > 16 an item takes one group of 16 of them, and with
+// G <= 8 one item takes two adjacent KV heads), so each K/V byte is read
+// from HBM once for every 16 heads.  Keys
 // are processed in tiles of 16 (one MFMA M-tile); block_size is a multiple
 // of 16, so a tile never straddles two cache blocks.
 //

@@ -19,13 +19,22 @@
 // registers hold data in transit.  Each wave fetches 64 / NW consecutive key
 // rows of a tile; they lie in one 16-key group, hence in one cache block, so
 // a wave needs one block-table entry per tile, fetched a tile before its K/V.
-// Rows are stored unpadded with the 16-byte pieces of row R permuted
-// (piece c at slot c ^ (R & 7) for K, c ^ 2 (R & 3) for V): the K operand
-// reads (16 bytes of 8 rows at a time) and the V transpose reads
-// (ds_read_b64_tr_b16, 32 bytes of 4 rows per 16 lanes) each hit distinct
-// banks.  Rows at or past the sequence end are fetched as a copy of its
-// last row (finite, masked), so block-table padding and poisoned tails are
-// never touched.
+// Rows are stored unpadded with the 16-byte pieces of row R permuted (for
+// D = 128, piece c at slot c ^ (R & 15) for K and c ^ 4 (R & 3) for V; see
+// swz_k / swz_v): the K operand reads (16 rows at one piece index per 16
+// lanes) and the V transpose reads (ds_read_b64_tr_b16, 4 rows x 4 pieces
+// per 32 lanes) each cover all 64 banks.  Rows at or past the sequence end
+// are fetched as a copy of its last row (finite, masked), so block-table
+// padding and poisoned tails are never touched.
+//
+// The grid is a compact list of the query tiles (at most one empty slot per
+// sequence), found by a wave-parallel search over cu_seqlens_q.  A
+// workgroup's key tiles run in three parts: tiles that may cut a row's
+// visible range run the masked code; the tiles all its rows see run the
+// unmasked code two per pass, so each tile's ring stage (and the LDS read
+// offsets) are constants.  An fp8 cache with an fp8 query computes S^T on
+// the fp8 MFMA (32x32x64) straight from the staged codes; otherwise fp8
+// tiles are widened to 16 bits in LDS first.
 //
 // Softmax work per score is kept to max, one fma, exp2, add and half a
 // packed convert: the scale is folded into the exponent, masks are applied
