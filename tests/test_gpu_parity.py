@@ -337,6 +337,24 @@ def test_prefill_noncausal_alibi(pa, runner, D, Hq, Hkv, ctx, q):
     assert_lse_close(res[0][0].lse, ref[1], "non-causal alibi lse")
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,ctx,q,wl,cap", [(128, 8, 2, [64, 0, 300], [100, 29, 170], 50, 0.0),
+                                                    (64, 12, 3, [17, 400], [150, 66], 0, 10.0)])
+def test_prefill_noncausal_window(pa, runner, D, Hq, Hkv, ctx, q, wl, cap):
+    """Non-causal prefill with a sliding window: a query at p sees keys
+    p - window_left .. L - 1 (the window bounds only the left side), with
+    and without softcap; window_left 0 leaves the query's own key and every
+    later one."""
+    _announce(f"prefill non-causal window {wl} D={D} Hq={Hq} Hkv={Hkv}")
+    w = W.custom(f"noncausal_window_d{D}", 17, ctx, q, Hq, Hkv, D, 16, torch.bfloat16, "prefill",
+                 window_left=wl, softcap=cap)
+    w.steps[0].calls[0].causal = False
+    cache, res = runner.run_workload(w)
+    kc, vc = oracle_cache(w, 0)
+    ref = oracle_call(w, kc, vc, w.steps[0].calls[0])
+    assert_attn_close(res[0][0].out, ref[0], "non-causal window")
+    assert_lse_close(res[0][0].lse, ref[1], "non-causal window lse")
+
+
 def test_block_table_padding_never_read(pa, runner):
     """Entries past a sequence's last block point at a spare block of the
     pool whose K/V are NaN: a kernel that read through padding would show it
