@@ -94,7 +94,7 @@ def test_reshape_and_cache_padding_strides_negative_slots(pa, dtype, D, Hkv, ali
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("pdt,odt", [(torch.float32, torch.bfloat16), (torch.float32, torch.float32),
                                      (torch.bfloat16, torch.bfloat16), (torch.float16, torch.float16)])
-@pytest.mark.parametrize("S,D", [(2, 128), (32, 256), (5, 64)])
+@pytest.mark.parametrize("S,D", [(2, 128), (32, 256), (5, 64), (9, 128), (70, 128)])
 def test_merge_attn_states(pa, pdt, odt, S, D):
     _announce(f"merge S={S} D={D} {pdt}->{odt}")
     g = torch.Generator().manual_seed(S * D)
