@@ -569,8 +569,7 @@ def run_cascade(args, pa, B=64, P=4096, suffix_range=(64, 1024)):
     out_c = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
     out_d = torch.empty_like(out_c)
     ws = (torch.empty(17, B, Hq, D, dtype=torch.bfloat16, device="cuda"),
-          torch.empty(17, Hq, B, dtype=torch.float32, device="cuda"),
-          torch.empty(B + 3, dtype=torch.int32, device="cuda"))
+          torch.empty(17, Hq, B, dtype=torch.float32, device="cuda"))
     po = torch.empty(S, B, Hq, D, dtype=torch.float32, device="cuda")
     pl = torch.empty(S, Hq, B, dtype=torch.float32, device="cuda")
     mx = int(lens.max())

@@ -321,16 +321,20 @@ int merge_attn_states(void* out, float* out_lse, const void* parts_out,
  *                      every block-table row are the same blocks, and every
  *                      sequence's queries come after the prefix
  *                      (seq_len - query_len >= common_prefix_len).
- *   max_prefix_splits  1..255: the prefix pass may split the prefix keys
- *                      into up to this many parts (it does when there are
- *                      few queries, as in a decode batch, so that the pass
- *                      fills the GPU); the workspaces hold that many parts
- *                      plus one;
+ *   max_prefix_splits  1..255: the workspaces hold max_prefix_splits + 1
+ *                      partial results.  The prefix pass may split the
+ *                      prefix keys into up to max_prefix_splits parts (it
+ *                      does when there are few queries, as in a decode
+ *                      batch, so that the pass fills the GPU); the suffix
+ *                      pass may split each sequence's own keys into up to 4
+ *                      (when there are few sequences), the prefix then
+ *                      taking correspondingly fewer;
  *   parts_out          workspace [max_prefix_splits + 1, total_q, num_heads,
- *                      head_size] of dtype (prefix parts, then the suffix);
+ *                      head_size] of dtype (prefix parts, then the suffix
+ *                      parts);
  *   parts_lse          fp32 workspace [max_prefix_splits + 1, num_heads,
  *                      total_q];
- *   work_ints          int32 workspace [num_seqs + 3].
+ *   work_ints          reserved, nullable, not accessed.
  *   Workspaces are caller-owned and overwritten; num_kv_heads * (total_q +
  *   num_seqs) must be below 2^31.
  */
@@ -377,8 +381,8 @@ int scaled_fp8_quant(void* out, const void* input, const float* scale,
  * library's two paths on MI355X (paged_attn_decode with splits +
  * merge_attn_states against paged_attn_cascade), calibrated on measured
  * times of decode batches of 8..128 requests with 256..8192 shared keys:
- * fixed costs, unique and re-read K/V bytes, the prefix pass's MFMA work
- * and the longest per-request suffix.
+ * fixed costs, unique and re-read K/V bytes, the prefix pass's MFMA work,
+ * the longest per-request suffix per suffix part and a cost per request.
  *
  *   query_lens, seq_lens  HOST int32 [num_reqs]: new queries and keys
  *                         (including the prefix) of each request.

@@ -413,7 +413,7 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
                        v_scale: Optional[torch.Tensor] = None,
                        q_scale: Optional[torch.Tensor] = None) -> None:
     """Causal prefill over a shared prefix (see paged_attn_cascade in the
-    header).  ``workspace`` is (parts_out, parts_lse, work_ints) sized for
+    header).  ``workspace`` is (parts_out, parts_lse) sized for
     max_prefix_splits + 1 parts; it is allocated here with torch when not
     given."""
     _need("out", out, _ATTN, contiguous=True)
@@ -431,17 +431,17 @@ def paged_attn_cascade(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tens
     if workspace is None:
         n = max_prefix_splits + 1
         workspace = (torch.empty(n, t, hq, d, dtype=out.dtype, device=q.device),
-                     torch.empty(n, hq, t, dtype=torch.float32, device=q.device),
-                     torch.empty(b + 3, dtype=torch.int32, device=q.device))
-    parts_out, parts_lse, ints = workspace
+                     torch.empty(n, hq, t, dtype=torch.float32, device=q.device))
+    parts_out, parts_lse = workspace
     _need("workspace parts_out", parts_out, (out.dtype,), contiguous=True)
     _need("workspace parts_lse", parts_lse, _F32, contiguous=True)
-    _need("workspace ints", ints, _INT32, contiguous=True)
+    if parts_out.shape[0] < max_prefix_splits + 1 or parts_lse.shape[0] < max_prefix_splits + 1:
+        raise ValueError("paged_attn_cascade: the workspace must hold max_prefix_splits + 1 parts")
     _check("paged_attn_cascade", lib.paged_attn_cascade(
         _ptr(out), _ptr(lse), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q),
         _ptr(seq_lens), _ptr(block_table), block_table.stride(0), b, t, int(max_seqlen_q),
         int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), float(softcap), _ptr(sinks),
-        int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), _ptr(ints),
+        int(common_prefix_len), int(max_prefix_splits), _ptr(parts_out), _ptr(parts_lse), None,
         _code(out.dtype), _code(key_cache.dtype), _ptr(k_scale), _ptr(v_scale), _ptr(q_scale),
         _stream(stream)))
 

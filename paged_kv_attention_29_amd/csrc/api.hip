@@ -474,8 +474,8 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
   if (max_prefix_splits < 1 || max_prefix_splits > 255)
     return fail(PA_ERR_INVALID, "%s: max_prefix_splits must be in [1, 255] (got %d)", fn,
                 max_prefix_splits);
-  if (num_seqs > 0 && (cu_seqlens_q == nullptr || parts_out == nullptr || parts_lse == nullptr ||
-                       work_ints == nullptr))
+  (void)work_ints;  // reserved: the passes need no device-side lengths
+  if (num_seqs > 0 && (cu_seqlens_q == nullptr || parts_out == nullptr || parts_lse == nullptr))
     return fail(PA_ERR_INVALID, "%s: NULL cu_seqlens_q or workspace", fn);
   if (num_heads / num_kv_heads > 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 128 query heads per KV head", fn);
@@ -520,7 +520,7 @@ int paged_attn_cascade(void* out, float* lse, const void* q, const void* key_cac
   p.v_scale = v_scale;
   p.q_scale = q_scale;
   return hip_result(pa::launch_cascade(p, common_prefix_len, max_prefix_splits, parts_out,
-                                       parts_lse, work_ints, static_cast<hipStream_t>(stream)),
+                                       parts_lse, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

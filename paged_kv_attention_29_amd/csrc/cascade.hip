@@ -7,13 +7,14 @@
 //      0), non-causal — every query comes after the prefix — split over the
 //      prefix keys when there are few queries;
 //   2. each sequence's queries over its keys after the prefix, causal,
-//      through block_table + prefix_blocks with lengths seq_lens - prefix;
-//   3. merge_attn_states of the prefix parts and the suffix part.
+//      through block_table + prefix_blocks with lengths seq_lens - prefix,
+//      split over those keys when there are few sequences;
+//   3. merge_attn_states of the prefix parts and the suffix parts.
 //
-// Steps 1-2 are the prefill kernel and step 3 the merge kernel; a small
-// kernel first writes the device-side lengths the two prefill launches
-// read (cu = {0, T}, {prefix}, and the suffix lengths) into the caller's
-// integer workspace.
+// Steps 1-2 are the prefill kernel and step 3 the merge kernel.  The prefix
+// pass reads its one sequence's bounds as cu_seqlens_q[0], cu_seqlens_q[B]
+// and min(seq_lens[0], prefix); the suffix pass subtracts the prefix from
+// seq_lens as it reads them; so no device-side lengths are prepared.
 #include "common.h"
 #include "launch.h"
 
@@ -21,72 +22,80 @@ namespace pa {
 
 namespace {
 
-__global__ __launch_bounds__(256) void cascade_setup_kernel(const int32_t* seq_lens, int num_seqs,
-                                                            int total_q, int prefix,
-                                                            int32_t* ints) {
-  const int i0 = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i0 == 0) {
-    ints[0] = 0;
-    ints[1] = total_q;
-    ints[2] = prefix;
-  }
-  for (int i = i0; i < num_seqs; i += gridDim.x * blockDim.x) ints[3 + i] = seq_lens[i] - prefix;
-}
-
 size_t elem_bytes(Dtype t) { return t == kF32 ? 4 : 2; }
+
+// Keys per split (a multiple of 64) when a pass over up to `keys` keys is
+// split into at most `max_parts` parts so that its grid of `wgs` workgroups
+// grows to about 512; 0 = no split.  *parts receives the number of parts.
+int key_split_for(int64_t wgs, int keys, int max_parts, int* parts) {
+  const int tiles = (keys + 63) / 64;
+  int s = static_cast<int>((512 + wgs - 1) / wgs);
+  s = s > max_parts ? max_parts : s;
+  s = s > tiles ? tiles : s;
+  s = s < 1 ? 1 : s;
+  const int ks = 64 * ((tiles + s - 1) / s);
+  *parts = (keys + ks - 1) / ks;
+  return *parts > 1 ? ks : 0;
+}
 
 }  // namespace
 
 int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void* parts_out,
-                   float* parts_lse, int32_t* ints, hipStream_t stream) {
+                   float* parts_lse, hipStream_t stream) {
   const int64_t T = p.total_q;
-  const unsigned grid = static_cast<unsigned>(p.num_seqs / 256 + 1 > 1024 ? 1024 : p.num_seqs / 256 + 1);
-  hipLaunchKernelGGL(cascade_setup_kernel, dim3(grid), dim3(256), 0, stream, p.seq_lens,
-                     p.num_seqs, static_cast<int>(T), prefix, ints);
-  if (hipGetLastError() != hipSuccess) return -3;
+  const int budget = max_prefix_splits + 1;  // parts the workspaces hold
+  const int tok_per_tile = 128 / (p.num_heads / p.num_kv_heads);  // 128 MFMA rows per tile
+
+  // Suffix pass: with few sequences its grid has only Hkv * (T / tokens-per-
+  // tile + B) workgroups, each walking its sequence's whole suffix one tile
+  // at a time, so the longest suffix sets the pass's time; its keys are then
+  // split too, into at most 4 parts (more measured slower: the extra parts
+  // cost the merge and the prefix pass more than they save), leaving the
+  // prefix at least one.
+  const int suf_keys = p.max_seqlen_k - prefix;
+  int suf_parts = 1;
+  const int suf_split = key_split_for((int64_t)p.num_kv_heads * (T / tok_per_tile + p.num_seqs),
+                                      suf_keys, budget - 1 < 4 ? budget - 1 : 4, &suf_parts);
 
   // Prefix pass: every query over the shared prefix, non-causal.  With few
   // queries (a decode batch) its grid would have only Hkv * T / tokens-per-
   // tile workgroups, so the prefix keys are split (in 64-key tiles) until
-  // the pass has about 512 workgroups; split z writes part z.
-  const int tok_per_tile = 128 / (p.num_heads / p.num_kv_heads);  // 128 MFMA rows per tile
-  const int64_t wgs = (int64_t)p.num_kv_heads * ((T + tok_per_tile - 1) / tok_per_tile);
-  const int tiles = (prefix + 63) / 64;
-  int splits = static_cast<int>((512 + wgs - 1) / wgs);
-  splits = splits < 1 ? 1 : splits;
-  splits = splits > max_prefix_splits ? max_prefix_splits : splits;
-  splits = splits > tiles ? tiles : splits;
-  const int key_split = 64 * ((tiles + splits - 1) / splits);
-  splits = (prefix + key_split - 1) / key_split;
+  // the pass has about 512 workgroups, in the parts the suffix left.
+  int pre_parts = 1;
+  const int pre_split = key_split_for((int64_t)p.num_kv_heads * ((T + tok_per_tile - 1) / tok_per_tile),
+                                      prefix, budget - suf_parts, &pre_parts);
 
   AttnParams pre = p;
   pre.out = parts_out;
   pre.lse = parts_lse;
-  pre.cu_seqlens_q = ints;
-  pre.seq_lens = ints + 2;
+  // one sequence: queries [cu[0], cu[B]) = [0, T), keys min(seq_lens[0],
+  // prefix) = prefix
+  pre.cu_step = p.num_seqs;
+  pre.len_cap = prefix;
   pre.num_seqs = 1;
   pre.max_seqlen_q = static_cast<int>(T);
   pre.max_seqlen_k = prefix;
   pre.causal = 0;
-  pre.key_split = splits > 1 ? key_split : 0;  // sinks (if any) join split 0
+  pre.key_split = pre_split;  // sinks (if any) join split 0
   int rc = launch_prefill(pre, stream);
   if (rc != 0) return rc;
 
   // Suffix pass: each sequence over its own keys after the prefix, causal,
-  // into part `splits`
+  // into parts pre_parts ..
   AttnParams suf = p;
-  suf.out = static_cast<char*>(parts_out) + splits * T * p.num_heads * p.head_size * elem_bytes(p.dtype);
-  suf.lse = parts_lse + splits * T * p.num_heads;
-  suf.seq_lens = ints + 3;
+  suf.out = static_cast<char*>(parts_out) + pre_parts * T * p.num_heads * p.head_size * elem_bytes(p.dtype);
+  suf.lse = parts_lse + pre_parts * T * p.num_heads;
+  suf.len_sub = prefix;
   suf.block_table = p.block_table + prefix / p.block_size;
-  suf.max_seqlen_k = p.max_seqlen_k - prefix;
+  suf.bt_cols = p.block_table_stride - prefix / p.block_size;
+  suf.max_seqlen_k = suf_keys;
   suf.causal = 1;
-  suf.key_split = 0;
+  suf.key_split = suf_split;
   suf.sinks = nullptr;  // counted once, in the prefix part
   rc = launch_prefill(suf, stream);
   if (rc != 0) return rc;
 
-  return launch_merge(p.out, p.lse, parts_out, parts_lse, splits + 1, T, p.num_heads,
+  return launch_merge(p.out, p.lse, parts_out, parts_lse, pre_parts + suf_parts, T, p.num_heads,
                       p.head_size, p.dtype, p.dtype, stream);
 }
 
@@ -98,27 +107,36 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
 //   plain split decode + merge: a fixed cost, the K/V bytes each key is
 //     read for once (HBM), and the re-reads of the shared prefix by the
 //     other requests (served mostly by the caches);
-//   cascade: a fixed cost (four launches), the prefix pass's MFMA work,
-//     the prefix bytes, the suffix bytes, and the longest suffix (the suffix
-//     pass runs one query per sequence, so its time follows its longest
-//     item).
+//   cascade: a fixed cost (three launches), the prefix pass's MFMA work,
+//     the prefix bytes, the suffix bytes, the longest suffix per suffix
+//     part (a suffix-pass workgroup walks its part of one sequence's keys
+//     tile by tile), and a cost per request (the suffix pass's workgroups,
+//     the merge's rows).  The suffix parts are those launch_cascade takes
+//     with the binding's default of 16 prefix splits.
 // Returns true when the modelled cascade time is the lower one.
 bool cascade_beats_split_decode(int prefix, const int32_t* seq_lens, int num_reqs, int num_heads,
                                 int num_kv_heads, int head_size, int kv_elem_bytes) {
   const double row = (double)num_kv_heads * head_size * 2 * kv_elem_bytes;  // bytes per key
-  double suf_sum = 0, suf_max = 0;
+  double suf_sum = 0;
+  int suf_max = 0;
   for (int b = 0; b < num_reqs; ++b) {
-    const double s = seq_lens[b] > prefix ? seq_lens[b] - prefix : 0;
+    const int s = seq_lens[b] > prefix ? seq_lens[b] - prefix : 0;
     suf_sum += s;
     suf_max = s > suf_max ? s : suf_max;
   }
+  const int tok_per_tile = 128 / (num_heads / num_kv_heads);
+  int suf_parts = 1;
+  if (suf_max > 0)
+    key_split_for((int64_t)num_kv_heads * (num_reqs / tok_per_tile + num_reqs), suf_max, 4,
+                  &suf_parts);
   const double MB = 1e6;
   const double unique = (prefix + suf_sum) * row / MB;
   const double reread = (double)(num_reqs - 1) * prefix * row / MB;
   const double gflop = 4.0 * head_size * num_heads * (double)num_reqs * prefix / 1e9;
-  const double t_plain = 14.702 + 0.17726 * unique + 0.10315 * reread;
-  const double t_cascade = 20.284 + 1.1570 * gflop + 0.15095 * suf_sum * row / MB +
-                           3.3735 * suf_max * row / MB + 0.14465 * prefix * row / MB;
+  const double t_plain = 15.545 + 0.1768 * unique + 0.10296 * reread;
+  const double t_cascade = 17.527 + 0.91162 * gflop + 0.20213 * suf_sum * row / MB +
+                           0.27494 * suf_max * row / MB / suf_parts + 0.21763 * prefix * row / MB +
+                           0.047678 * num_reqs;
   return t_cascade < t_plain;
 }
 

@@ -65,6 +65,15 @@ struct AttnParams {
   int32_t* split_counters = nullptr;
   int num_splits;
   int key_split;  // prefill only: keys per split (a multiple of 64), 0 = none
+  // prefill only: sequence b's queries are [cu[b], cu[b + cu_step]) (0 =
+  // step 1) and its key count min(seq_lens[b] - len_sub, len_cap) (len_cap
+  // 0 = no cap); bt_cols > 0 bounds the block-table columns read from
+  // block_table (which may point into the rows), else block_table_stride
+  // does
+  int cu_step = 0;
+  int len_sub = 0;
+  int len_cap = 0;
+  int64_t bt_cols = 0;
   Dtype dtype;
 };
 
@@ -95,11 +104,11 @@ int launch_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
 int launch_prefill(const AttnParams& p, hipStream_t stream);
 // prefix-shared causal prefill (p.causal, no window / ALiBi): parts_out
 // [max_prefix_splits + 1, T, Hq, D] in p.dtype, parts_lse
-// [max_prefix_splits + 1, Hq, T], ints [num_seqs + 3]
+// [max_prefix_splits + 1, Hq, T], shared by the prefix and suffix passes
 // host: the calibrated time comparison behind pa_use_cascade (decode batches)
 bool cascade_beats_split_decode(int prefix, const int32_t* seq_lens, int num_reqs, int num_heads,
                                 int num_kv_heads, int head_size, int kv_elem_bytes);
 int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void* parts_out,
-                   float* parts_lse, int32_t* ints, hipStream_t stream);
+                   float* parts_lse, hipStream_t stream);
 
 }  // namespace pa

@@ -73,6 +73,13 @@ struct PrefillArgs {
   const int32_t* block_table;
   int64_t bt_stride;
   int64_t total_q;
+  // block-table columns readable from block_table (bt_stride, or fewer when
+  // block_table points into the rows, past a shared prefix)
+  int64_t bt_cols;
+  // sequence c's queries are [cu_q[c], cu_q[c + cu_step]) (cu_step 1, or B
+  // for the whole batch as one sequence) and its key count is
+  // min(seq_lens[c] - len_sub, len_cap)
+  int cu_step, len_sub, len_cap;
   int B, Hq, Hkv, G, bs, tok_per_tile;
   uint32_t bs_magic;
   float scale_log2;     // scale * log2(e)
@@ -317,9 +324,9 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     const bool in = lane * step < span;
     const bool fin = in && step == 1;
     const int cq = in ? a.cu_q[c] : 0;
-    const int cq1 = fin ? a.cu_q[c + 1] : 0;
-    const int cl = fin ? a.seq_lens[c] : 0;
-    const int cb = fin && wave_blk < a.bt_stride ? a.block_table[(int64_t)c * a.bt_stride + wave_blk] : 0;
+    const int cq1 = fin ? a.cu_q[c + a.cu_step] : 0;
+    const int cl = fin ? min(a.seq_lens[c] - a.len_sub, a.len_cap) : 0;
+    const int cb = fin && wave_blk < a.bt_cols ? a.block_table[(int64_t)c * a.bt_stride + wave_blk] : 0;
     const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in && cq / tok + c <= t));
     if (k == 0) {  // below S_0 (cu_q[0] > 0)
       if (wave == 0) trace_put(a.trace, kTrEntry, t_entry);
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   //      row, its own key being visible; only an empty key split has none.)
   static_assert(NST == 2, "the prologue fills one stage ahead");
   const int n = t_end - t_begin;
-  const bool early = n > 0 && t_begin == 0 && wave * RW <= L - 1 && wave_blk < a.bt_stride;
+  const bool early = n > 0 && t_begin == 0 && wave * RW <= L - 1 && wave_blk < a.bt_cols;
   if (early) issue_tile(t_begin, blk0, 0);
   // (loaded unconditionally, an in-range entry even without tiles, so that
   // ids has one definition up to its claim after the prologue's wait: a
@@ -998,6 +1005,10 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.block_table = p.block_table;
   a.bt_stride = p.block_table_stride;
   a.total_q = p.total_q;
+  a.bt_cols = p.bt_cols > 0 ? p.bt_cols : p.block_table_stride;
+  a.cu_step = p.cu_step > 0 ? p.cu_step : 1;
+  a.len_sub = p.len_sub;
+  a.len_cap = p.len_cap > 0 ? p.len_cap : INT_MAX;
   a.B = p.num_seqs;
   a.Hq = p.num_heads;
   a.Hkv = p.num_kv_heads;

@@ -182,7 +182,7 @@ def _cascade(pa, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(prefix=0), -1), (dict(prefix=24), -1), (dict(prefix=80), -1), (dict(parts=None), -1),
-    (dict(ints=None), -1), (dict(parts_lse=None), -1), (dict(cu=None), -1), (dict(out=None), -1),
+    (dict(parts_lse=None), -1), (dict(cu=None), -1), (dict(out=None), -1),
     (dict(d=96), -2), (dict(dtype=2), -2), (dict(bs=20), -1), (dict(cap=-1.0), -1),
     (dict(max_splits=0), -1), (dict(max_splits=256), -1),
 ])

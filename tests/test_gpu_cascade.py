@@ -55,12 +55,17 @@ CASES = [
     ("g2_d64_fp16_cap", 64, [17, 1, 90], [3, 0, 50], 4, 2, 64, 32, torch.float16, 5.0),
     ("g1_d256", 32, [40, 9], [10, 100], 2, 2, 256, 16, torch.bfloat16, 0.0),
     # decode batches: one query per sequence, so the prefix pass splits its
-    # keys and the suffix pass is the split decode
+    # keys (and, with at most a few hundred sequences, the suffix pass too)
     ("decode_q1_splits", 1024, [1] * 40, list(range(3, 43 * 7, 7)), 32, 8, 128, 16,
      torch.bfloat16, 0.0),
     ("decode_q1_g8_d256_cap", 512, [1] * 9, [0, 1, 15, 16, 17, 300, 511, 900, 64], 16, 2, 256,
      32, torch.float16, 30.0),
     ("decode_q1_g1_d64", 128, [1] * 70, list(range(0, 70 * 13, 13)), 4, 4, 64, 16,
+     torch.bfloat16, 0.0),
+    # few sequences with long suffixes: the suffix pass splits their keys
+    # (4 parts of 384; 3 of 512 with max_prefix_splits 3), so the queries of
+    # the short suffixes see only split 0 and the other parts are empty
+    ("few_seqs_long_suffixes", 128, [3, 70, 1, 20], [900, 40, 1500, 0], 8, 2, 128, 16,
      torch.bfloat16, 0.0),
 ]
 
