@@ -381,8 +381,9 @@ int scaled_fp8_quant(void* out, const void* input, const float* scale,
  * library's two paths on MI355X (paged_attn_decode with splits +
  * merge_attn_states against paged_attn_cascade), calibrated on measured
  * times of decode batches of 8..128 requests with 256..8192 shared keys:
- * fixed costs, unique and re-read K/V bytes, the prefix pass's MFMA work,
- * the longest per-request suffix per suffix part and a cost per request.
+ * fixed costs, unique and re-read K/V bytes, the prefix pass's MFMA work
+ * and a cost per request.  (On every measured batch the cascade was the
+ * faster path, so there the decision is the support checks'.)
  *
  *   query_lens, seq_lens  HOST int32 [num_reqs]: new queries and keys
  *                         (including the prefix) of each request.

@@ -11,7 +11,8 @@
 //      split over those keys when there are few sequences;
 //   3. merge_attn_states of the prefix parts and the suffix parts.
 //
-// Steps 1-2 are the prefill kernel and step 3 the merge kernel.  The prefix
+// Steps 1-2 are one launch of the prefill kernel (two problems in one grid)
+// and step 3 the merge kernel.  The prefix
 // pass reads its one sequence's bounds as cu_seqlens_q[0], cu_seqlens_q[B]
 // and min(seq_lens[0], prefix); the suffix pass subtracts the prefix from
 // seq_lens as it reads them; so no device-side lengths are prepared.
@@ -77,8 +78,6 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
   pre.max_seqlen_k = prefix;
   pre.causal = 0;
   pre.key_split = pre_split;  // sinks (if any) join split 0
-  int rc = launch_prefill(pre, stream);
-  if (rc != 0) return rc;
 
   // Suffix pass: each sequence over its own keys after the prefix, causal,
   // into parts pre_parts ..
@@ -92,7 +91,15 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
   suf.causal = 1;
   suf.key_split = suf_split;
   suf.sinks = nullptr;  // counted once, in the prefix part
-  rc = launch_prefill(suf, stream);
+
+  // Both passes in one launch, the suffix pass's workgroups first: the
+  // prefix pass's short workgroups then fill the slots the suffix pass's
+  // uneven ones free (one launch by one when they cannot share a grid).
+  int rc = launch_prefill_pair(suf, pre, stream);
+  if (rc == 1) {
+    rc = launch_prefill(pre, stream);
+    if (rc == 0) rc = launch_prefill(suf, stream);
+  }
   if (rc != 0) return rc;
 
   return launch_merge(p.out, p.lse, parts_out, parts_lse, pre_parts + suf_parts, T, p.num_heads,
@@ -107,36 +114,27 @@ int launch_cascade(const AttnParams& p, int prefix, int max_prefix_splits, void*
 //   plain split decode + merge: a fixed cost, the K/V bytes each key is
 //     read for once (HBM), and the re-reads of the shared prefix by the
 //     other requests (served mostly by the caches);
-//   cascade: a fixed cost (three launches), the prefix pass's MFMA work,
-//     the prefix bytes, the suffix bytes, the longest suffix per suffix
-//     part (a suffix-pass workgroup walks its part of one sequence's keys
-//     tile by tile), and a cost per request (the suffix pass's workgroups,
-//     the merge's rows).  The suffix parts are those launch_cascade takes
-//     with the binding's default of 16 prefix splits.
-// Returns true when the modelled cascade time is the lower one.
+//   cascade: a fixed cost (two launches), the prefix pass's MFMA work,
+//     the prefix bytes, the suffix bytes, and a cost per request (the
+//     suffix pass's workgroups, the merge's rows).  The longest suffix per
+//     suffix part was a candidate term too; the fit gives it no weight in
+//     the measured range (the suffix split and the prefix pass sharing the
+//     launch hide it).
+// On every measured batch the cascade was the faster path, so within that
+// range the decision is the support checks'.  Returns true when the
+// modelled cascade time is the lower one.
 bool cascade_beats_split_decode(int prefix, const int32_t* seq_lens, int num_reqs, int num_heads,
                                 int num_kv_heads, int head_size, int kv_elem_bytes) {
   const double row = (double)num_kv_heads * head_size * 2 * kv_elem_bytes;  // bytes per key
   double suf_sum = 0;
-  int suf_max = 0;
-  for (int b = 0; b < num_reqs; ++b) {
-    const int s = seq_lens[b] > prefix ? seq_lens[b] - prefix : 0;
-    suf_sum += s;
-    suf_max = s > suf_max ? s : suf_max;
-  }
-  const int tok_per_tile = 128 / (num_heads / num_kv_heads);
-  int suf_parts = 1;
-  if (suf_max > 0)
-    key_split_for((int64_t)num_kv_heads * (num_reqs / tok_per_tile + num_reqs), suf_max, 4,
-                  &suf_parts);
+  for (int b = 0; b < num_reqs; ++b) suf_sum += seq_lens[b] > prefix ? seq_lens[b] - prefix : 0;
   const double MB = 1e6;
   const double unique = (prefix + suf_sum) * row / MB;
   const double reread = (double)(num_reqs - 1) * prefix * row / MB;
   const double gflop = 4.0 * head_size * num_heads * (double)num_reqs * prefix / 1e9;
-  const double t_plain = 15.545 + 0.1768 * unique + 0.10296 * reread;
-  const double t_cascade = 17.527 + 0.91162 * gflop + 0.20213 * suf_sum * row / MB +
-                           0.27494 * suf_max * row / MB / suf_parts + 0.21763 * prefix * row / MB +
-                           0.047678 * num_reqs;
+  const double t_plain = 15.585 + 0.17556 * unique + 0.10298 * reread;
+  const double t_cascade = 14.157 + 0.95417 * gflop + 0.17501 * suf_sum * row / MB +
+                           0.17287 * prefix * row / MB + 0.066596 * num_reqs;
   return t_cascade < t_plain;
 }
 

@@ -102,6 +102,11 @@ int launch_check_indices(const int64_t* slot_mapping, int64_t num_tokens,
                          int num_seqs, int64_t num_blocks, int block_size, int32_t* counts,
                          hipStream_t stream);
 int launch_prefill(const AttnParams& p, hipStream_t stream);
+// two independent prefill problems of the same variant (dtype, head size,
+// cache and query types, softcap; no ALiBi) in one launch, p0's workgroups
+// first; returns 1 without launching when they cannot share one (the
+// caller then launches them one by one), else 0 or a negative code
+int launch_prefill_pair(const AttnParams& p0, const AttnParams& p1, hipStream_t stream);
 // prefix-shared causal prefill (p.causal, no window / ALiBi): parts_out
 // [max_prefix_splits + 1, T, Hq, D] in p.dtype, parts_lse
 // [max_prefix_splits + 1, Hq, T], shared by the prefix and suffix passes

@@ -57,7 +57,7 @@ namespace {
 constexpr int kKT = 64;       // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4, kQ8 = 8 };
+enum { kSoftcap = 1, kAlibi = 2, kFp8 = 4, kQ8 = 8, kDual = 16 };
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -103,6 +103,18 @@ struct PrefillArgs {
   const float* q_scale;
   // timeline trace records (trace library only), or null
   uint64_t* trace;
+  // workgroups along x of this problem's grid (key splits along z)
+  int grid_x;
+};
+
+// A launch's arguments: one problem (p[0]), or, in the kDual variants, two
+// independent problems in one grid: workgroups [0, n0) run p[0], the rest
+// p[1], each numbered x fastest then z as in its own grid.  (The cascade
+// runs its suffix and prefix passes this way, so that the short prefix
+// workgroups fill the slots the suffix pass's uneven ones leave.)
+struct PrefillLaunch {
+  PrefillArgs p[2];
+  int n0;
 };
 
 // Four waves (one per SIMD) per workgroup and a two-stage K/V ring, so
@@ -250,7 +262,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <typename T, int D, int FEAT>
-__global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(PrefillLaunch launch) {
+  constexpr bool DUAL = FEAT & kDual;
+  // this workgroup's problem and its place in that problem's grid
+  const int sel = DUAL && blockIdx.x >= static_cast<unsigned>(launch.n0) ? 1 : 0;
+  PrefillArgs a = launch.p[sel];
+  const unsigned lin = DUAL ? blockIdx.x - (sel ? launch.n0 : 0) : 0;
+  const unsigned bx = DUAL ? lin % static_cast<unsigned>(a.grid_x) : blockIdx.x;
+  const unsigned bz = DUAL ? lin / static_cast<unsigned>(a.grid_x) : blockIdx.z;
   constexpr bool SOFTCAP = FEAT & kSoftcap;
   constexpr bool ALIBI = FEAT & kAlibi;
   constexpr bool F8 = FEAT & kFp8;
@@ -307,8 +326,8 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   // works through one sequence's query tiles together and the sequence's
   // K/V for that head stays in the XCD's L2 while they run.  Inside a
   // sequence the long (late) tiles go first.
-  const int g = blockIdx.x % a.Hkv;
-  const int t = static_cast<int>(blockIdx.x / a.Hkv);
+  const int g = bx % a.Hkv;
+  const int t = static_cast<int>(bx / a.Hkv);
   const int tok = a.tok_per_tile;
   // The last b with S_b <= t, by a wave-parallel search: each round splits
   // the candidate range [lo, lo + span) into 64 parts and keeps the last
@@ -367,8 +386,8 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   int k_hi = a.causal ? min(L, p_last + 1) : L;
   int k_lo = a.window_left >= 0 ? max(0, p_first - a.window_left) : 0;
   if (a.key_split > 0) {
-    k_lo = max(k_lo, static_cast<int>(blockIdx.z) * a.key_split);
-    k_hi = min(k_hi, static_cast<int>(blockIdx.z + 1) * a.key_split);
+    k_lo = max(k_lo, static_cast<int>(bz) * a.key_split);
+    k_hi = min(k_hi, static_cast<int>(bz + 1) * a.key_split);
   }
   const int t_begin = k_lo / kKT;
   const int t_end = max((k_hi + kKT - 1) / kKT, t_begin);  // empty split: no tile
@@ -886,7 +905,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   // ---- epilogue: lane holds O^T[d = dc*32 + 8*(e/4) + 4*g2 + e%4][row]
   float l_tot = l_run + shfl_xor(l_run, 32);
   float m_fin = m_run, o_scale = 1.0f;
-  if (a.sinks != nullptr && blockIdx.z == 0) {
+  if (a.sinks != nullptr && bz == 0) {
     // the sink as one more state (max sk, sum 1, output 0)
     const float sk = a.sinks[head] * kLog2e;
     const float M = fmaxf(m_run, sk);
@@ -897,7 +916,7 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
     }
   }
   const float inv = l_tot > 0.f ? o_scale * v_scale * __builtin_amdgcn_rcpf(l_tot) : 0.0f;
-  const int64_t part = blockIdx.z;  // key split (0 without splits)
+  const int64_t part = bz;  // key split (0 without splits)
   // The wave's 32 output rows go through LDS (the ring is idle: every wave
   // passed the loop's last barrier and no DMA is in flight) so that the
   // global stores write whole rows, 16 bytes per lane: stored straight from
@@ -945,8 +964,19 @@ __global__ __launch_bounds__(kNW<D> * 64, kMinWG<D>) void prefill_kernel(Prefill
   }
 }
 
+// One problem of a launch: its arguments, its longest query run (0 = no
+// work) and its number of key splits.
+struct Problem {
+  PrefillArgs a;
+  int max_seqlen_q;
+  int n_ksplits;
+};
+
+// Launches prefill_kernel<T, D, FEAT> over n problems (1, or 2 with kDual).
+// Returns 0, -3 on a HIP error, or 1 when two problems do not fit one grid
+// (the caller then launches them one by one).
 template <typename T, int D, int FEAT>
-int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream_t stream) {
+int launch_p(const Problem* pr, int n, hipStream_t stream) {
   // the LDS limit of this kernel, raised once per device (the attribute is
   // per device; concurrent first calls may both set it, which is harmless)
   static std::atomic<uint64_t> attr_set{0};
@@ -959,42 +989,81 @@ int launch_p(const PrefillArgs& args, int max_seqlen_q, int n_ksplits, hipStream
       return -3;
     attr_set.fetch_or(uint64_t(1) << dev);
   }
-  PrefillArgs a = args;
-  a.tok_per_tile = kRows<D> / a.G;
-  if (max_seqlen_q == 0) return 0;
-  // the compact tile list: floor(total_q / tokens per tile) + B slots per
-  // KV head (the API bounds Hkv * (total_q + B) below 2^31)
-  const int64_t slots = a.total_q / a.tok_per_tile + a.B;
-  const int splits = a.key_split > 0 ? n_ksplits : 1;
-  const dim3 grid(static_cast<unsigned>(a.Hkv * slots), 1, static_cast<unsigned>(splits));
+  PrefillLaunch L{};
+  uint64_t wgs[2] = {0, 0};
+  int splits[2] = {1, 1};
+  for (int i = 0; i < n; ++i) {
+    if (pr[i].max_seqlen_q == 0) {
+      if (n == 1) return 0;
+      return 1;
+    }
+    PrefillArgs a = pr[i].a;
+    a.tok_per_tile = kRows<D> / a.G;
+    // the compact tile list: floor(total_q / tokens per tile) + B slots per
+    // KV head (the API bounds Hkv * (total_q + B) below 2^31)
+    const int64_t slots = a.total_q / a.tok_per_tile + a.B;
+    a.grid_x = static_cast<int>(a.Hkv * slots);
+    splits[i] = a.key_split > 0 ? pr[i].n_ksplits : 1;
+    wgs[i] = static_cast<uint64_t>(a.grid_x) * splits[i];
+    L.p[i] = a;
+  }
+  dim3 grid(static_cast<unsigned>(L.p[0].grid_x), 1, static_cast<unsigned>(splits[0]));
+  if (n == 2) {
+    if (wgs[0] + wgs[1] > (uint64_t(1) << 22)) return 1;
+    L.n0 = static_cast<int>(wgs[0]);
+    grid = dim3(static_cast<unsigned>(wgs[0] + wgs[1]), 1, 1);
+  }
   hipLaunchKernelGGL((prefill_kernel<T, D, FEAT>), grid, dim3(kNW<D> * 64),
-                     (prefill_lds_bytes<D, (FEAT & kFp8) != 0>()), stream, a);
+                     (prefill_lds_bytes<D, (FEAT & kFp8) != 0>()), stream, L);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <typename T, int D, int F8>
-int launch_feat(const PrefillArgs& a, int mq, int ns, bool softcap, bool alibi, hipStream_t s) {
-  if (softcap && alibi) return launch_p<T, D, F8 | kSoftcap | kAlibi>(a, mq, ns, s);
-  if (softcap) return launch_p<T, D, F8 | kSoftcap>(a, mq, ns, s);
-  if (alibi) return launch_p<T, D, F8 | kAlibi>(a, mq, ns, s);
-  return launch_p<T, D, F8>(a, mq, ns, s);
+// The kernel variant for a call's features, handed to fn as Inst<T, D, FEAT>
+// (X: extra feature bits; kDual variants exist without ALiBi only).
+template <typename T_, int D_, int FEAT_>
+struct Inst {
+  using T = T_;
+  static constexpr int D = D_;
+  static constexpr int FEAT = FEAT_;
+};
+
+template <typename T, int D, int X, typename Fn>
+int by_feat(bool softcap, bool alibi, Fn& fn) {
+  if constexpr (X & kDual) {
+    if (alibi) return -3;
+  } else {
+    if (softcap && alibi) return fn(Inst<T, D, X | kSoftcap | kAlibi>{});
+    if (alibi) return fn(Inst<T, D, X | kAlibi>{});
+  }
+  if (softcap) return fn(Inst<T, D, X | kSoftcap>{});
+  return fn(Inst<T, D, X>{});
 }
 
-template <typename T, int F8>
-int launch_t(const PrefillArgs& a, int D, int mq, int ns, bool softcap, bool alibi,
-             hipStream_t s) {
+template <typename T, int X, typename Fn>
+int by_head_size(int D, bool softcap, bool alibi, Fn& fn) {
   switch (D) {
-    case 64: return launch_feat<T, 64, F8>(a, mq, ns, softcap, alibi, s);
-    case 128: return launch_feat<T, 128, F8>(a, mq, ns, softcap, alibi, s);
-    default: return launch_feat<T, 256, F8>(a, mq, ns, softcap, alibi, s);
+    case 64: return by_feat<T, 64, X>(softcap, alibi, fn);
+    case 128: return by_feat<T, 128, X>(softcap, alibi, fn);
+    default: return by_feat<T, 256, X>(softcap, alibi, fn);
   }
 }
 
-}  // namespace
+template <int X, typename Fn>
+int by_variant(const AttnParams& p, Fn& fn) {
+  const bool softcap = p.softcap > 0.f, alibi = p.alibi_slopes != nullptr;
+  const bool bf16 = p.dtype == kBF16;
+  if (p.kv_fp8 && p.q_scale != nullptr)
+    return bf16 ? by_head_size<BF16, X | kFp8 | kQ8>(p.head_size, softcap, alibi, fn)
+                : by_head_size<F16, X | kFp8 | kQ8>(p.head_size, softcap, alibi, fn);
+  if (p.kv_fp8)
+    return bf16 ? by_head_size<BF16, X | kFp8>(p.head_size, softcap, alibi, fn)
+                : by_head_size<F16, X | kFp8>(p.head_size, softcap, alibi, fn);
+  return bf16 ? by_head_size<BF16, X>(p.head_size, softcap, alibi, fn)
+              : by_head_size<F16, X>(p.head_size, softcap, alibi, fn);
+}
 
-int launch_prefill(const AttnParams& p, hipStream_t stream) {
-  if (p.num_seqs == 0 || p.total_q == 0) return 0;
-  PrefillArgs a;
+Problem make_problem(const AttnParams& p) {
+  PrefillArgs a{};
   a.out = static_cast<uint16_t*>(p.out);
   a.lse = p.lse;
   a.q = static_cast<const uint16_t*>(p.q);
@@ -1030,20 +1099,33 @@ int launch_prefill(const AttnParams& p, hipStream_t stream) {
   a.q_scale = p.q_scale;
   a.trace = trace_buffer();
   const int ns = p.key_split > 0 ? (p.max_seqlen_k + p.key_split - 1) / p.key_split : 1;
-  const bool alibi = p.alibi_slopes != nullptr;
-  if (p.kv_fp8 && p.q_scale != nullptr) {
-    if (p.dtype == kBF16)
-      return launch_t<BF16, kFp8 | kQ8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
-    return launch_t<F16, kFp8 | kQ8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
-  }
-  if (p.kv_fp8) {
-    if (p.dtype == kBF16)
-      return launch_t<BF16, kFp8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
-    return launch_t<F16, kFp8>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
-  }
-  if (p.dtype == kBF16)
-    return launch_t<BF16, 0>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
-  return launch_t<F16, 0>(a, p.head_size, p.max_seqlen_q, ns, softcap, alibi, stream);
+  return Problem{a, p.max_seqlen_q, ns};
+}
+
+}  // namespace
+
+int launch_prefill(const AttnParams& p, hipStream_t stream) {
+  if (p.num_seqs == 0 || p.total_q == 0) return 0;
+  const Problem pr = make_problem(p);
+  auto fn = [&](auto inst) {
+    using I = decltype(inst);
+    return launch_p<typename I::T, I::D, I::FEAT>(&pr, 1, stream);
+  };
+  return by_variant<0>(p, fn);
+}
+
+int launch_prefill_pair(const AttnParams& p0, const AttnParams& p1, hipStream_t stream) {
+  if (p0.num_seqs == 0 || p0.total_q == 0 || p1.num_seqs == 0 || p1.total_q == 0) return 1;
+  if (p0.dtype != p1.dtype || p0.head_size != p1.head_size || p0.kv_fp8 != p1.kv_fp8 ||
+      (p0.q_scale != nullptr) != (p1.q_scale != nullptr) || (p0.softcap > 0.f) != (p1.softcap > 0.f) ||
+      p0.alibi_slopes != nullptr || p1.alibi_slopes != nullptr)
+    return 1;
+  const Problem pr[2] = {make_problem(p0), make_problem(p1)};
+  auto fn = [&](auto inst) {
+    using I = decltype(inst);
+    return launch_p<typename I::T, I::D, I::FEAT>(pr, 2, stream);
+  };
+  return by_variant<kDual>(p0, fn);
 }
 
 }  // namespace pa

@@ -56,10 +56,11 @@ def test_dcp_disables(pa):
 
 def test_non_decode_batches_take_the_cascade(pa):
     """As on the page: without split-KV decode (a request with several
-    queries, or one query head per KV head) the cascade is chosen."""
+    queries, or one query head per KV head) the cascade is chosen; so is a
+    small decode batch, where it was measured faster too."""
     ql = np.ones(8, np.int32)
     sl = np.full(8, 300, np.int32)
-    assert not _use(pa, 256, ql, sl)        # a small decode batch: split decode is faster
+    assert _use(pa, 256, ql, sl)
     ql2 = ql.copy()
     ql2[3] = 2
     assert _use(pa, 256, ql2, sl)
@@ -87,9 +88,8 @@ def test_invalid_arguments(pa):
 def test_measured_crossover(pa):
     """On the measured decode batches (32/8/128 bf16, requests 8..128,
     prefixes 256..8192, suffix ranges 1-64 and 64-1024) the rule picks the
-    path that was faster on all but a few near-ties and noisy small batches:
-    the time lost by its choice averages under 2% and is at most 25% at any
-    point."""
+    path that was faster, up to a few near-ties: the time lost by its
+    choice averages under 2% and is at most 25% at any point."""
     rows = []
     for line in open(PROFILE):
         m = re.match(r"\| (\d+) \| (\d+) \| (\d+)-(\d+) \| (\d+) \| (\d+) \| ([\d.]+) \| ([\d.]+) \|", line)
@@ -105,5 +105,5 @@ def test_measured_crossover(pa):
         pick = _use(pa, P, np.ones(B, np.int32), (P + suf).astype(np.int32))
         agree += pick == (t_cas < t_plain)
         lost.append((t_cas if pick else t_plain) / min(t_cas, t_plain) - 1)
-    assert agree >= 50
+    assert agree >= 55
     assert np.mean(lost) < 0.02 and max(lost) < 0.25
