@@ -108,3 +108,33 @@ def test_cascade_matches_oracle_and_prefill(pa, case):
     assert_attn_close(out3, ro, f"{name} cascade, at most 3 prefix splits")
     assert_attn_close(out1, ro, f"{name} cascade, one prefix part")
     assert_lse_close(lse1, rl, f"{name} cascade lse, one prefix part")
+
+
+@pytest.mark.parametrize("B,P,lo,hi", [(64, 4096, 64, 1024), (8, 1024, 64, 1024)],
+                         ids=["b64_prefix4096", "b8_prefix1024"])
+def test_cascade_decode_batches_at_bench_size(pa, B, P, lo, hi):
+    """The decode batches the cascade is timed on (32 query / 8 KV heads of
+    128, bf16, block 16; each request's own history drawn from [lo, hi]
+    with numpy PCG64(6), as in the bench): 64 requests over 4096 shared keys
+    (16 prefix parts, the suffix pass unsplit, both passes in one launch),
+    and 8 requests over 1024 (the suffix pass split 4 ways).  Every output
+    and LSE against the oracle's cascade, which equals plain causal
+    attention."""
+    print(f"\n[gpu-case] cascade decode batch B={B} P={P} suffix {lo}-{hi}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(6))
+    suffix = rng.integers(lo, hi, size=B, endpoint=True)
+    q, kc, vc, cu, lens, table = _case(B + P, P, [1] * B, [int(s) - 1 for s in suffix], 32, 8, 128,
+                                       16, torch.bfloat16)
+    assert lens == [P + int(s) for s in suffix]
+    scale = 128 ** -0.5
+    dev = dict(device="cuda")
+    T = B
+    out = torch.full((T, 32, 128), float("nan"), dtype=torch.bfloat16, **dev)
+    lse = torch.full((32, T), float("nan"), dtype=torch.float32, **dev)
+    pa.paged_attn_cascade(out, q.cuda(), kc.cuda(), vc.cuda(), torch.tensor(cu, dtype=torch.int32, **dev),
+                          torch.tensor(lens, dtype=torch.int32, **dev), table.cuda(), 1, max(lens),
+                          scale, P, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.cascade(q, kc, vc, cu, lens, table, scale, P)
+    assert_attn_close(out, ro, f"cascade B={B} P={P}")
+    assert_lse_close(lse, rl, f"cascade lse B={B} P={P}")
