@@ -12,10 +12,10 @@
 //   3. merge_attn_states of the prefix parts and the suffix parts.
 //
 // Steps 1-2 are one launch of the prefill kernel (two problems in one grid)
-// and step 3 the merge kernel.  The prefix
-// pass reads its one sequence's bounds as cu_seqlens_q[0], cu_seqlens_q[B]
-// and min(seq_lens[0], prefix); the suffix pass subtracts the prefix from
-// seq_lens as it reads them; so no device-side lengths are prepared.
+// and step 3 the merge kernel.  The prefix pass reads its one sequence's
+// bounds as cu_seqlens_q[0], cu_seqlens_q[B] and min(seq_lens[0], prefix);
+// the suffix pass subtracts the prefix from seq_lens as it reads them; so
+// no device-side lengths are prepared.
 #include "common.h"
 #include "launch.h"
 
